@@ -1,0 +1,27 @@
+"""CPU oracle for MLA speculative-decoding verify attention (test infrastructure).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may use
+this package; the product path never imports it. Every function is plain
+fp64 numpy (or pure Python for the brute force) and shares no code with the
+GPU implementation.
+
+Parity status: every function here is pinned by the CPU test suite against
+closed forms, invariants, a pure-Python brute force and torch's
+scaled_dot_product_attention in fp64; none is "parity unpinned".
+"""
+
+from .attention import (  # noqa: F401
+    LATENT,
+    VALUE,
+    decode_bf16,
+    sequence_offsets,
+    gather_latents,
+    visibility,
+    masked_softmax_rows,
+    verify_attention,
+    partial_attention,
+    lse_merge,
+    split_merge_attention,
+    online_softmax_attention,
+    brute_force,
+)
