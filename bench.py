@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark: MLA speculative-decoding verify attention on one MI355X.
+
+One step = one verify_attn() call (plan + split + merge kernels) over the
+long-context workload: 1 sequence, 64 heads, 16 verify positions in a causal
+chain, prefix 185,000, page_size 1 with shuffled kv_indices into a 512k-slot
+pool, bf16 N(0,1) latents, q = 0.5 N(0,1), scale 1/sqrt(192). Inputs are
+seeded and synthetic and are resident in HBM before timing starts.
+
+Before each timed call a 1 GiB fill evicts the caches (the 256 MiB last-level
+cache would otherwise hold most of the 213 MB KV working set); call and split
+kernel times come from HIP events on the call's stream. The JSON line reports
+us/call (lower is better), algorithmic HBM GB/s against 8 TB/s, the split
+kernel's MFMA roofline fraction, and the fp64 CPU oracle timed on a bounded
+sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verify-attn µs/call + achieved HBM GB/s (% of peak), 64 heads, 185k prefix"
+PEAK_HBM = 8.0e12            # MI355X HBM3E, bytes/s
+PEAK_MFMA_BF16 = 2.5e15      # MI355X dense bf16/fp16 MFMA, FLOP/s
+FLOP_PER_PAIR = 2 * (576 + 512)   # q.k over 576 dims + p*v over 512 dims, per visible (row, key)
+KERNEL_SRC = os.path.join(ROOT, "speculative_decoding_verify_03_amd", "csrc", "verify_attn_kernels.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "split_kernel_long185k_pmc.json")
+
+WORKLOAD_TEXT = {
+    "long185k": "B=1 H=64 Q=16 prefix=185000 causal chain; page_size 1, kv_indices = first 185016 of a "
+                "seeded permutation of a 524288-slot pool; bf16 latents N(0,1), q 0.5*N(0,1), scale 1/sqrt(192)",
+    "long185k_h8": "B=1 H=8 Q=16 prefix=185000 causal chain (per-rank shape of 8-way head sharding); "
+                   "524288-slot pool, shuffled kv_indices; bf16 N(0,1), q 0.5*N(0,1)",
+    "p4k": "B=1 H=64 Q=16 prefix=4096 causal chain, contiguous kv_indices; bf16 N(0,1)",
+    "tree32k": "B=1 H=64 Q=16 prefix=32768 random draft tree (depth<=8), 262144-slot pool, shuffled",
+    "batch8": "B=8 H=64 Q=8 prefixes U[1024,131072], random draft trees, 2097152-slot pool, shuffled",
+    "tiny": "B=1 H=8 Q=4 prefix=256 causal chain, 1024-slot pool, shuffled",
+}
+
+
+def algorithmic_bytes(w) -> int:
+    """HBM bytes a perfect implementation moves once: KV rows, indices, q, mask, lengths, out, lse."""
+    B, Q, H = w.B, w.Q, w.H
+    kv = int(w.total_kv) * 1152
+    return (kv + w.total_kv * 4 + B * Q * H * 1152 + B * Q * Q + B * 4
+            + B * Q * H * 512 * 4 + B * Q * H * 4)
+
+
+def visible_pairs(w) -> int:
+    """Number of visible (query-head row, key) pairs."""
+    tot = 0
+    for b in range(w.B):
+        P = int(w.prefix_lens[b])
+        per_query = P + w.tree_mask[b].astype(np.int64).sum(axis=1)
+        tot += int(per_query.sum()) * w.H
+    return tot
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per split launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source (else None)."""
+    try:
+        with open(PMC_SUMMARY) as f:
+            s = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if s.get("kernel_sha") != kernel_sha():
+        return None
+    return s.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w, heads, reps=1):
+    """The fp64 oracle (as is) on a head subset of the same workload, scaled to one call."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = None
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.verify_attention(w.q, w.kv_pool, w.kv_indices, w.prefix_lens, w.tree_mask, w.scale,
+                                heads=heads)
+    dt = (time.perf_counter() - t0) / reps
+    scale_up = w.H / len(heads)
+    what = "all heads" if len(heads) == w.H else f"heads {heads} of {w.H}, scaled by {scale_up:g}"
+    return {
+        "value": round(dt * scale_up * 1e6, 1),
+        "unit": "µs/call",
+        "cores": blas_threads if blas_threads else len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": f"oracle.verify_attention on the same workload ({what}), {reps} repetitions, "
+                  f"{dt:.2f} s each; host has {len(os.sched_getaffinity(0))} usable cores",
+    }
+
+
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 3) -> None:
+    """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="long185k", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting fill between calls")
+    ap.add_argument("--chunk", type=int, default=0, help="keys-per-chunk override (0 = automatic)")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the one-GPU value is the per-GPU share; sharding is described in the design notes)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+
+    import speculative_decoding_verify_03_amd as va
+    from workloads import make_config
+
+    print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
+    w = make_config(args.config)
+    dev = torch.device("cuda:0")
+    q = torch.from_numpy(w.q.view(np.int16)).to(dev)
+    kv = torch.from_numpy(w.kv_pool.view(np.int16)).to(dev)
+    idx = torch.from_numpy(w.kv_indices).to(dev)
+    pl = torch.from_numpy(w.prefix_lens).to(dev)
+    tm = torch.from_numpy(w.tree_mask).to(dev)
+    va.set_chunk_override(args.chunk)
+    plan = va.query_plan(w.B, w.Q, w.H, w.total_kv)
+    ws = va.alloc_workspace(w.B, w.Q, w.H, w.total_kv, device=dev)
+    out = torch.empty((w.B, w.Q, w.H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.Q, w.H), dtype=torch.float32, device=dev)
+    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    scale = float(w.scale)
+
+    def call():
+        va.verify_attn(q, kv, idx, pl, tm, scale, out=out, lse=lse, workspace=ws)
+
+    print(f"[bench] plan {plan}; warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+
+    def timed(n, do_flush):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+        for e in ev:          # torch creates the HIP events on first record; the split
+            e[2].record()     # pair is then re-recorded by the library around the kernel
+            e[3].record()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(n):
+            if do_flush:
+                flush.zero_()
+            va.set_split_events(ev[k][2], ev[k][3])
+            ev[k][0].record()
+            call()
+            ev[k][1].record()
+        va.set_split_events(None, None)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        calls = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3   # us
+        splits = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e3
+        return calls, splits, wall
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    calls, splits, wall = timed(args.steps, flush is not None)
+    warm_calls, warm_splits, _ = timed(args.steps, False)
+
+    us = float(calls.mean())
+    abytes = algorithmic_bytes(w)
+    flops = visible_pairs(w) * FLOP_PER_PAIR
+    split_us = float(splits.mean())
+    achieved_tflops = flops / (split_us * 1e-6) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(us, 2),
+        "unit": "µs/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: {WORKLOAD_TEXT[args.config]}",
+                   "plan": plan, "cache_flush_between_calls": flush is not None},
+        "hbm_gbps": round(abytes / (us * 1e-6) / 1e9, 1),
+        "hbm_frac": round(abytes / (us * 1e-6) / PEAK_HBM, 4),
+        "algorithmic_bytes": abytes,
+        "algorithmic_flops": flops,
+        "us_per_call_median": round(float(np.median(calls)), 2),
+        "us_per_call_warm": round(float(warm_calls.mean()), 2),
+        "split_kernel_us": round(split_us, 2),
+        "split_kernel_us_warm": round(float(warm_splits.mean()), 2),
+        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved_tflops, 1),
+            "peak": PEAK_MFMA_BF16 / 1e12,
+            "unit": "TFLOP/s",
+            "frac": round(achieved_tflops * 1e12 / PEAK_MFMA_BF16, 4),
+            "traffic": measured_traffic(),
+            "kernel": "split_kernel",
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, heads=list(range(w.H)), reps=2)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

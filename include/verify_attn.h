@@ -1,0 +1,143 @@
+/*
+ * verify_attn.h -- C ABI of the MI355X (gfx950) MLA speculative-decoding
+ * verify-attention library (libverify_attn.so).
+ *
+ * The operation (pages: "Building the paged sm120 verify kernel", section
+ * "What This Build Achieves: The paged+bf16 Kernel"; "The Build That
+ * Unlocked 3-6x Decode Speedup", section "The Context"):
+ *
+ *   For every sequence b, query position i and head h, attend with the
+ *   576-d query q[b][i][h] over the KV positions of sequence b. Position j
+ *   of sequence b lives in pool slot kv_indices[off_b + j] (page_size 1),
+ *   where off_b = sum_{b' < b} (prefix_lens[b'] + Q). The first
+ *   prefix_lens[b] positions (the prefix) are visible to every query; the
+ *   last Q positions are the speculative tail, and tail position t is
+ *   visible to query i iff tree_mask[b][i][t] != 0. Keys are the whole
+ *   576-d bf16 latent rows, values their first 512 dims, scores are
+ *   scale * (q . k), and
+ *       lse[b][i][h] = ln sum_{visible j} exp(score_j)
+ *       out[b][i][h] = sum_{visible j} exp(score_j - lse) * value_j.
+ *   A query with no visible position gets out = 0 and lse = -inf.
+ *
+ * The KV range of each sequence is split into chunks that run on separate
+ * workgroups (flash-decode with online softmax over KV tiles); a second
+ * kernel merges the chunk partials by log-sum-exp ("KV-split flash-decode",
+ * NSPLIT: page "The Build That Unlocked ...", section "The Context"; page
+ * "The Build Script Edit ...", section "Context").
+ *
+ * Conventions for every entry point:
+ *  - Device pointers are caller-owned device memory; the library allocates
+ *    nothing and never frees caller memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued asynchronously; no entry point synchronises, reads
+ *    device data on the host or allocates.
+ *  - Return value: VA_OK (0) or a negative va_status. On error nothing has
+ *    been enqueued (argument errors) or the launch failed (VA_EHIP);
+ *    verify_attn_last_error() then describes it. No C++ exception crosses
+ *    this interface.
+ *  - Results are deterministic: identical inputs give bitwise-identical
+ *    outputs (no floating-point atomics, fixed reduction order).
+ */
+#ifndef VERIFY_ATTN_H
+#define VERIFY_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VA_LATENT_DIM 576 /* key width: one compressed latent row, bf16 */
+#define VA_VALUE_DIM 512  /* value width: the leading dims of the same row */
+#define VA_MAX_Q 64       /* verify positions per sequence supported */
+
+typedef enum {
+  VA_OK = 0,
+  VA_EINVAL = -1, /* bad pointer, alignment or dimension; nothing enqueued */
+  VA_ENOSPC = -2, /* workspace smaller than verify_attn_workspace_size() */
+  VA_EHIP = -3    /* the HIP runtime reported an error for a launch */
+} va_status;
+
+/*
+ * Bytes of device workspace verify_attn() needs for these sizes on the
+ * current HIP device (the split plan depends on its compute-unit count).
+ * Returns 0 if the sizes are invalid.
+ */
+size_t verify_attn_workspace_size(int B, int Q, int H, int64_t total_kv);
+
+/*
+ * Verify attention (see the top of this file for the definition).
+ *
+ *  q           bf16 [B][Q][H][576], contiguous, 16-byte aligned.
+ *  kv_pool     bf16 [num_slots][576], row stride 1152 bytes, 16-byte aligned.
+ *  kv_indices  int32 [total_kv]: sequence b owns entries off_b .. off_b +
+ *              prefix_lens[b] + Q - 1, its prefix slots in position order
+ *              followed by the Q tail slots in query order. An entry outside
+ *              [0, num_slots) is read as an all-zero row (never a fault).
+ *  prefix_lens int32 [B] on the device, each >= 0 (a negative value counts as 0).
+ *  tree_mask   uint8 [B][Q][Q]; [b][i][t] != 0 iff query i sees tail position t
+ *              (normally the diagonal is set: a query sees its own draft token).
+ *  scale       multiplies q . k (in fp32, on the fp32 dot product).
+ *  out         fp32 [B][Q][H][512], 16-byte aligned (written).
+ *  lse         fp32 [B][Q][H], natural log (written).
+ *  B >= 1, 1 <= Q <= 64, H >= 1, num_slots >= 1,
+ *  total_kv = sum_b (prefix_lens[b] + Q), with B*Q <= total_kv < 2^31.
+ *  workspace   device memory of at least verify_attn_workspace_size(B, Q, H,
+ *              total_kv) bytes, 256-byte aligned; its contents on entry do
+ *              not matter and are scratch afterwards.
+ *
+ * Device-side preconditions that the host cannot check: the prefix_lens
+ * sum must match total_kv (positions past total_kv are treated as absent),
+ * inputs must be finite, and value elements must lie within the finite
+ * fp16 range (|v| < 65504), since the probability-times-value product runs
+ * in fp16 (see the design notes on precision).
+ */
+int verify_attn(const void* q, const void* kv_pool, const int32_t* kv_indices,
+                const int32_t* prefix_lens, const uint8_t* tree_mask, float scale,
+                float* out, float* lse, int B, int Q, int H, int64_t num_slots,
+                int64_t total_kv, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Thread-local description of the last error on this thread ("" if none). */
+const char* verify_attn_last_error(void);
+
+/*
+ * Test hook: runs the split kernel's own gather routine (kv_indices -> 16-byte
+ * direct-to-LDS loads -> LDS tile) for positions 0..n-1 and copies each tile
+ * back out in position order, so the gather can be compared bit-exactly with
+ * kv_pool[kv_indices[j]]. rows_out is bf16 [n][576], 16-byte aligned. Slots
+ * outside [0, num_slots) produce zero rows, as in verify_attn().
+ */
+int verify_attn_debug_gather(const void* kv_pool, const int32_t* kv_indices, int64_t n,
+                             int64_t num_slots, void* rows_out, void* stream);
+
+/*
+ * The split plan verify_attn() would use for these sizes on the current
+ * device: keys per chunk, the chunk capacity of the workspace, row tiles per
+ * sequence (128 query-head rows each) and the split-kernel grid size. Any
+ * output pointer may be NULL. Returns VA_OK or VA_EINVAL.
+ */
+int verify_attn_query_plan(int B, int Q, int H, int64_t total_kv, int32_t* chunk_keys,
+                           int32_t* max_chunks, int32_t* row_tiles, int32_t* grid);
+
+/*
+ * Profiling hook (thread-local): when both are non-NULL, every later
+ * verify_attn() call on this thread records start_event on its stream right
+ * before launching the split kernel and stop_event right after it, so the
+ * caller can time that kernel alone (events are hipEvent_t passed as void*,
+ * created and owned by the caller). Passing NULL, NULL turns it off.
+ */
+void verify_attn_set_split_events(void* start_event, void* stop_event);
+
+/*
+ * Process-wide override of the keys per chunk (rounded up to a multiple of 32;
+ * 0 restores the automatic choice). Meant for tuning sweeps; the workspace
+ * size depends on it, so query the size again after changing it.
+ */
+void verify_attn_set_chunk_override(int32_t chunk_keys);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VERIFY_ATTN_H */

@@ -1,0 +1,229 @@
+// C-ABI shim of libverify_attn.so: argument validation, the split plan,
+// workspace carving and the three launches (plan, split, merge). The ABI is
+// declared in include/verify_attn.h. No entry point allocates, synchronises
+// or reads device memory on the host.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "va_internal.hpp"
+#include "verify_attn.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local hipEvent_t g_split_start = nullptr;
+thread_local hipEvent_t g_split_stop = nullptr;
+std::atomic<int32_t> g_chunk_override{0};
+std::atomic<int> g_cu_count[64];
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return VA_OK;
+}
+
+// Compute units of the current device (cached per device ordinal).
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0) return cached;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+bool dims_ok(int B, int Q, int H, int64_t total_kv) {
+  if (B < 1 || Q < 1 || Q > VA_MAX_Q || H < 1) return false;
+  if ((int64_t)Q * H > (1 << 24)) return false;
+  if (total_kv < (int64_t)B * Q || total_kv > (int64_t)INT32_MAX - VA_MAX_Q) return false;
+  return true;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// The split plan. Workgroups are (chunk, 128-row tile) pairs and one
+// workgroup fills a compute unit (8 waves, ~156 KiB of LDS), so the batch is
+// cut into about floor(CUs / row_tiles) chunks of ~equal length; the plan
+// kernel then sizes each sequence's chunks from its own length.
+bool make_plan(int B, int Q, int H, int64_t total_kv, int ncu, va::Plan* p) {
+  if (!dims_ok(B, Q, H, total_kv)) return false;
+  const int64_t R = (int64_t)Q * H;
+  p->row_tiles = (int32_t)((R + va::kRowsPerWG - 1) / va::kRowsPerWG);
+  int64_t target = ncu / p->row_tiles;
+  if (target < 1) target = 1;
+  int64_t ideal = (total_kv + target - 1) / target;
+  const int32_t ov = g_chunk_override.load(std::memory_order_relaxed);
+  if (ov > 0) ideal = ov;
+  if (ideal < va::kMinChunk && ov <= 0) ideal = va::kMinChunk;
+  ideal = (ideal + va::kUnit - 1) / va::kUnit * va::kUnit;
+  p->target = (int32_t)target;
+  p->ideal_keys = (int32_t)ideal;
+  // Each sequence gets max(1, round(N_b / ideal)) chunks, so the batch never
+  // needs more than total_kv / ideal + B of them.
+  const int64_t max_chunks = total_kv / ideal + B + 1;
+  if (max_chunks > INT32_MAX / 8) return false;
+  p->max_chunks = (int32_t)max_chunks;
+  const int64_t grid = (max_chunks + 7) / 8 * 8 * p->row_tiles;
+  if (grid > INT32_MAX) return false;
+  p->grid = (int32_t)grid;
+  size_t off = 0;
+  p->off_seq = off;
+  off += sizeof(int64_t) * (size_t)(B + 1);
+  p->off_chunk = off;
+  off += sizeof(int32_t) * (size_t)(B + 1);
+  p->off_len = off;
+  off += sizeof(int32_t) * (size_t)B;
+  off = align_up(off, 256);
+  p->off_lse = off;
+  off += sizeof(float) * (size_t)max_chunks * (size_t)R;
+  off = align_up(off, 256);
+  p->off_o = off;
+  off += sizeof(float) * (size_t)max_chunks * (size_t)R * va::kValue;
+  p->bytes = align_up(off, 256);
+  return true;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+size_t verify_attn_workspace_size(int B, int Q, int H, int64_t total_kv) {
+  va::Plan p;
+  if (!make_plan(B, Q, H, total_kv, cu_count(), &p)) return 0;
+  return p.bytes;
+}
+
+int verify_attn_query_plan(int B, int Q, int H, int64_t total_kv, int32_t* chunk_keys,
+                           int32_t* max_chunks, int32_t* row_tiles, int32_t* grid) {
+  va::Plan p;
+  if (!make_plan(B, Q, H, total_kv, cu_count(), &p)) return fail(VA_EINVAL, "invalid sizes");
+  if (chunk_keys) *chunk_keys = p.ideal_keys;
+  if (max_chunks) *max_chunks = p.max_chunks;
+  if (row_tiles) *row_tiles = p.row_tiles;
+  if (grid) *grid = p.grid;
+  return ok();
+}
+
+void verify_attn_set_split_events(void* start_event, void* stop_event) {
+  g_split_start = static_cast<hipEvent_t>(start_event);
+  g_split_stop = static_cast<hipEvent_t>(stop_event);
+}
+
+void verify_attn_set_chunk_override(int32_t chunk_keys) {
+  g_chunk_override.store(chunk_keys > 0 ? chunk_keys : 0, std::memory_order_relaxed);
+}
+
+const char* verify_attn_last_error(void) { return g_last_error.c_str(); }
+
+int verify_attn(const void* q, const void* kv_pool, const int32_t* kv_indices,
+                const int32_t* prefix_lens, const uint8_t* tree_mask, float scale, float* out,
+                float* lse, int B, int Q, int H, int64_t num_slots, int64_t total_kv,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    if (!q || !kv_pool || !kv_indices || !prefix_lens || !tree_mask || !out || !lse || !workspace)
+      return fail(VA_EINVAL, "null pointer argument");
+    if (!aligned(q, 16) || !aligned(kv_pool, 16) || !aligned(out, 16))
+      return fail(VA_EINVAL, "q, kv_pool and out must be 16-byte aligned");
+    if (!aligned(kv_indices, 4) || !aligned(prefix_lens, 4) || !aligned(lse, 4))
+      return fail(VA_EINVAL, "kv_indices, prefix_lens and lse must be 4-byte aligned");
+    if (!aligned(workspace, 256)) return fail(VA_EINVAL, "workspace must be 256-byte aligned");
+    if (!dims_ok(B, Q, H, total_kv))
+      return fail(VA_EINVAL, "bad sizes: B=%d Q=%d H=%d total_kv=%lld (need B>=1, 1<=Q<=%d, H>=1, "
+                  "B*Q <= total_kv < 2^31)", B, Q, H, (long long)total_kv, VA_MAX_Q);
+    if (num_slots < 1 || num_slots > INT64_MAX / va::kRowBytes)
+      return fail(VA_EINVAL, "bad num_slots %lld", (long long)num_slots);
+    if (!std::isfinite(scale)) return fail(VA_EINVAL, "scale must be finite");
+    va::Plan p;
+    if (!make_plan(B, Q, H, total_kv, cu_count(), &p)) return fail(VA_EINVAL, "sizes too large to plan");
+    if (workspace_bytes < p.bytes)
+      return fail(VA_ENOSPC, "workspace of %zu bytes < %zu needed", workspace_bytes, p.bytes);
+
+    char* ws = static_cast<char*>(workspace);
+    auto* seq_off = reinterpret_cast<int64_t*>(ws + p.off_seq);
+    auto* chunk_off = reinterpret_cast<int32_t*>(ws + p.off_chunk);
+    auto* chunk_len = reinterpret_cast<int32_t*>(ws + p.off_len);
+    auto* part_lse = reinterpret_cast<float*>(ws + p.off_lse);
+    auto* part_o = reinterpret_cast<float*>(ws + p.off_o);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    hipError_t e = va::launch_plan(prefix_lens, seq_off, chunk_off, chunk_len, B, Q, total_kv,
+                                   p.ideal_keys, p.max_chunks, st);
+    if (e != hipSuccess) return fail(VA_EHIP, "plan launch: %s", hipGetErrorString(e));
+
+    va::SplitArgs a;
+    a.q = static_cast<const uint16_t*>(q);
+    a.kv_pool = static_cast<const char*>(kv_pool);
+    a.kv_indices = kv_indices;
+    a.prefix_lens = prefix_lens;
+    a.tree_mask = tree_mask;
+    a.seq_off = seq_off;
+    a.chunk_off = chunk_off;
+    a.chunk_len = chunk_len;
+    a.part_o = part_o;
+    a.part_lse = part_lse;
+    a.num_slots = num_slots;
+    a.total_kv = total_kv;
+    a.B = B;
+    a.Q = Q;
+    a.H = H;
+    a.R = Q * H;
+    a.row_tiles = p.row_tiles;
+    a.c_log2 = scale * 1.4426950408889634f;
+    const bool timed = g_split_start != nullptr && g_split_stop != nullptr;
+    if (timed && (e = hipEventRecord(g_split_start, st)) != hipSuccess)
+      return fail(VA_EHIP, "event record: %s", hipGetErrorString(e));
+    e = va::launch_split(a, p.grid, st);
+    if (e != hipSuccess) return fail(VA_EHIP, "split launch: %s", hipGetErrorString(e));
+    if (timed && (e = hipEventRecord(g_split_stop, st)) != hipSuccess)
+      return fail(VA_EHIP, "event record: %s", hipGetErrorString(e));
+
+    e = va::launch_merge(part_o, part_lse, chunk_off, out, lse, B, Q * H, st);
+    if (e != hipSuccess) return fail(VA_EHIP, "merge launch: %s", hipGetErrorString(e));
+    return ok();
+  } catch (...) {
+    return fail(VA_EHIP, "unexpected C++ exception");
+  }
+}
+
+int verify_attn_debug_gather(const void* kv_pool, const int32_t* kv_indices, int64_t n,
+                             int64_t num_slots, void* rows_out, void* stream) {
+  try {
+    if (n < 0 || n > (int64_t)INT32_MAX * 16) return fail(VA_EINVAL, "bad n %lld", (long long)n);
+    if (n == 0) return ok();
+    if (!kv_pool || !kv_indices || !rows_out) return fail(VA_EINVAL, "null pointer argument");
+    if (!aligned(kv_pool, 16) || !aligned(rows_out, 16) || !aligned(kv_indices, 4))
+      return fail(VA_EINVAL, "kv_pool/rows_out must be 16-byte and kv_indices 4-byte aligned");
+    if (num_slots < 1 || num_slots > INT64_MAX / va::kRowBytes)
+      return fail(VA_EINVAL, "bad num_slots %lld", (long long)num_slots);
+    hipError_t e = va::launch_debug_gather(kv_pool, kv_indices, n, num_slots, rows_out,
+                                           static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(VA_EHIP, "debug gather launch: %s", hipGetErrorString(e));
+    return ok();
+  } catch (...) {
+    return fail(VA_EHIP, "unexpected C++ exception");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Internal interface between the C-ABI shim (capi.cpp) and the HIP kernels
+// (verify_attn_kernels.hip). Not installed; not part of the public header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace va {
+
+constexpr int kLatent = 576;           // key width (bf16 elements per latent row)
+constexpr int kValue = 512;            // value width (leading dims of the row)
+constexpr int kRowBytes = kLatent * 2; // 1152 bytes per pool row
+constexpr int kUnit = 32;              // keys per LDS tile
+constexpr int kRowsPerWave = 32;       // query-head rows owned by one wave
+constexpr int kWaves = 4;              // waves per workgroup
+constexpr int kRowsPerWG = kRowsPerWave * kWaves;  // 128 rows per row tile
+constexpr int kMinChunk = 256;         // smallest chunk worth a workgroup (keys)
+
+// Host-side split plan (the device refines chunk sizes per sequence).
+struct Plan {
+  int32_t row_tiles;    // ceil(Q*H / 128)
+  int32_t target;       // chunks the device should aim for over the whole batch
+  int32_t ideal_keys;   // keys per chunk that would hit `target` exactly (multiple of 32)
+  int32_t max_chunks;   // capacity of the partial buffers (chunks)
+  int32_t grid;         // split-kernel workgroups
+  size_t off_seq;       // workspace byte offsets
+  size_t off_chunk;
+  size_t off_len;
+  size_t off_lse;
+  size_t off_o;
+  size_t bytes;         // total workspace bytes
+};
+
+struct SplitArgs {
+  const uint16_t* q;
+  const char* kv_pool;
+  const int32_t* kv_indices;
+  const int32_t* prefix_lens;
+  const uint8_t* tree_mask;
+  const int64_t* seq_off;
+  const int32_t* chunk_off;
+  const int32_t* chunk_len;
+  float* part_o;
+  float* part_lse;
+  int64_t num_slots;
+  int64_t total_kv;
+  int32_t B, Q, H, R, row_tiles;
+  float c_log2;  // scale * log2(e)
+};
+
+hipError_t launch_plan(const int32_t* prefix_lens, int64_t* seq_off, int32_t* chunk_off,
+                       int32_t* chunk_len, int B, int Q, int64_t total_kv, int ideal_keys,
+                       int max_chunks, hipStream_t stream);
+hipError_t launch_split(const SplitArgs& a, int grid, hipStream_t stream);
+hipError_t launch_merge(const float* part_o, const float* part_lse, const int32_t* chunk_off,
+                        float* out, float* lse, int B, int R, hipStream_t stream);
+hipError_t launch_debug_gather(const void* kv_pool, const int32_t* kv_indices, int64_t n,
+                               int64_t num_slots, void* rows_out, hipStream_t stream);
+
+}  // namespace va

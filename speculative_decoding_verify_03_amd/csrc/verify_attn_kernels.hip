@@ -1,0 +1,565 @@
+// HIP kernels for MLA speculative-decoding verify attention on gfx950 (MI355X).
+//
+// Method (pages: "The Build That Unlocked 3-6x Decode Speedup", section "The
+// Context"; "Building the paged sm120 verify kernel", section "What This Build
+// Achieves"): flash-decode. The KV positions of each sequence are cut into
+// chunks; every (chunk, 128-row tile) pair is one workgroup that streams its
+// chunk through LDS in 32-key tiles with an online softmax, and a second
+// kernel merges the chunk partials by log-sum-exp.
+//
+// gfx950 mapping, per workgroup (4 waves, one per SIMD, 128 query-head rows):
+//  * gather: every 32-key tile is brought into LDS with 16-byte direct
+//    global->LDS loads through kv_indices (page_size 1, 1152-byte rows); a
+//    4-deep ring of tiles keeps three tiles in flight;
+//  * scores: S^T = K Q^T on MFMA 32x32x16 bf16. K comes from LDS (A operand),
+//    the wave's 32 query rows stay resident in VGPRs (B operand). All heads
+//    and verify positions of the tile share every latent row that is loaded;
+//  * softmax: each lane owns one row, so the running max / sum need only one
+//    cross-half exchange per tile; rescaling is lazy (only when a row max
+//    grows by more than 2^8);
+//  * values: O^T += V^T P^T on MFMA 32x32x16 fp16. P^T is taken straight
+//    from the score accumulators (no data movement), V^T is read from the same
+//    LDS tile with the gfx950 transpose read ds_read_b64_tr_b16 and converted
+//    bf16 -> fp16 in registers. P is fp16 (not bf16) for accuracy: fp16 keeps
+//    11 significant bits against bf16's 8.
+//
+// LDS tile layout (one 32-key tile, 36 KiB): 72 "chunk columns" of 16 bytes
+// (8 latent dims) x 32 key slots. Chunk c of key k sits at slot
+// (c * 32 + (k ^ 4 * (c & 1))) * 16; the xor keeps the transpose reads of V
+// at the 2-way minimum for 512-byte wave accesses.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "va_internal.hpp"
+
+namespace va {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kChunks = kRowBytes / 16;          // 72 chunk columns per row
+constexpr int kTileBytes = kUnit * kRowBytes;    // 36864 bytes per tile
+constexpr int kRing = 4;                         // tiles resident in LDS
+constexpr int kKSteps = kLatent / 16;            // 36 MFMA k-steps over the latent
+constexpr int kDvBlocks = kValue / 32;           // 16 value blocks of 32 dims
+constexpr int kLoadsPerWave = kChunks / 2 / kWaves;  // 9 wave-wide 1 KiB loads per tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazyRescale = 8.0f;             // log2 headroom before O is rescaled
+
+// An all-zero latent row: the gather source for absent positions, so LDS
+// never holds anything but finite data and a masked key contributes 0 * 0.
+__device__ __attribute__((aligned(16))) uint32_t g_zero_row[kRowBytes / 4] = {0};
+
+// Byte offset of (chunk column, key) inside one LDS tile.
+__device__ __forceinline__ int tile_offset(int chunk, int key) {
+  return (chunk * kUnit + (key ^ ((chunk & 1) << 2))) * 16;
+}
+
+// Key that lane `lane` fetches for every 1 KiB load of a tile: load q of the
+// tile writes chunks 2q and 2q+1; lane l lands at slot (2q + l/32, l%32).
+__device__ __forceinline__ int gather_key(int lane) { return (lane & 31) ^ ((lane >> 5) << 2); }
+
+// Issue this wave's share (9 x 1 KiB) of one tile gather. `slot` is the pool
+// row of gather_key(lane) (or any out-of-range value for an absent position).
+__device__ __forceinline__ void issue_tile_gather(const char* kv_pool, int64_t num_slots, int64_t slot,
+                                                  LDS_AS char* tile, int wave, int lane) {
+  const char* row = (slot >= 0 && slot < num_slots) ? kv_pool + slot * (int64_t)kRowBytes
+                                                    : reinterpret_cast<const char*>(g_zero_row);
+  row += (lane >> 5) * 16;
+#pragma unroll
+  for (int i = 0; i < kLoadsPerWave; ++i) {
+    const int ld = wave * kLoadsPerWave + i;
+    __builtin_amdgcn_global_load_lds(row + ld * 32, tile + ld * 1024, 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ LDS_AS char* lds_cast(char* p) { return (LDS_AS char*)(p); }
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+template <int I>
+struct IntC {
+  static constexpr int value = I;
+};
+// Calls f(IntC<0>{}) ... f(IntC<N-1>{}): compile-time loop indices for code
+// that needs them as immediates (instruction offsets).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IntC<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// ds_read_b64_tr_b16 issued as inline assembly. The compiler would otherwise
+// put a full vmcnt(0) in front of it (it cannot tell that the read does not
+// alias the direct-to-LDS loads still in flight), draining the gather
+// prefetch. The caller waits for the result with an explicit lgkmcnt.
+template <int kOffset>
+__device__ __forceinline__ u32x2 tr16_read(unsigned lds_addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "i"(kOffset));
+  return r;
+}
+
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
+
+// bf16 x 4 (as raw bits, two per dword) -> fp16 x 4; exact for |v| in the
+// fp16 normal range.
+__device__ __forceinline__ void bf16x4_to_f16(u32x2 v, f16x8& dst, int base) {
+  const unsigned lo = v[0];
+  const unsigned hi = v[1];
+  const float a0 = __builtin_bit_cast(float, lo << 16);
+  const float a1 = __builtin_bit_cast(float, lo & 0xffff0000u);
+  const float a2 = __builtin_bit_cast(float, hi << 16);
+  const float a3 = __builtin_bit_cast(float, hi & 0xffff0000u);
+  dst[base + 0] = (_Float16)a0;
+  dst[base + 1] = (_Float16)a1;
+  dst[base + 2] = (_Float16)a2;
+  dst[base + 3] = (_Float16)a3;
+}
+
+// ---------------------------------------------------------------------------
+// Plan: per-sequence KV offsets, balanced chunk lengths and chunk offsets.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) plan_kernel(const int32_t* __restrict__ prefix_lens,
+                                                   int64_t* __restrict__ seq_off,
+                                                   int32_t* __restrict__ chunk_off,
+                                                   int32_t* __restrict__ chunk_len, int B, int Q,
+                                                   int64_t total_kv, int ideal_keys, int max_chunks) {
+  __shared__ int64_t s_n[256];
+  __shared__ int32_t s_c[256];
+  const int tid = threadIdx.x;
+  int64_t carry_n = 0;
+  int32_t carry_c = 0;
+  for (int base = 0; base < B; base += 256) {
+    const int i = base + tid;
+    int64_t nb = 0;
+    int32_t cb = 0;
+    if (i < B) {
+      int64_t p = prefix_lens[i];
+      p = p < 0 ? 0 : (p > total_kv ? total_kv : p);
+      nb = p + Q;
+      // round(N_b / ideal) chunks, at least one; then equal 32-key-aligned lengths
+      int64_t n = (nb + ideal_keys / 2) / ideal_keys;
+      if (n < 1) n = 1;
+      int64_t len = (nb + n - 1) / n;
+      len = (len + kUnit - 1) / kUnit * kUnit;
+      cb = (int32_t)((nb + len - 1) / len);
+      chunk_len[i] = (int32_t)len;
+    }
+    s_n[tid] = nb;
+    s_c[tid] = cb;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int64_t an = tid >= off ? s_n[tid - off] : 0;
+      const int32_t ac = tid >= off ? s_c[tid - off] : 0;
+      __syncthreads();
+      s_n[tid] += an;
+      s_c[tid] += ac;
+      __syncthreads();
+    }
+    if (i < B) {
+      seq_off[i] = carry_n + s_n[tid] - nb;
+      const int32_t co = carry_c + s_c[tid] - cb;
+      chunk_off[i] = co < max_chunks ? co : max_chunks;
+    }
+    carry_n += s_n[255];
+    carry_c += s_c[255];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    seq_off[B] = carry_n;
+    chunk_off[B] = carry_c < max_chunks ? carry_c : max_chunks;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split kernel: one workgroup per (chunk, 128-row tile).
+//
+// 8 waves, two per SIMD. Waves 2j and 2j+1 form pair j and own the same 32
+// query-head rows; wave half p = wave & 1 computes the partial scores over
+// latent dims [288p, 288p + 288) and accumulates value dims [256p, 256p + 256).
+// The two partial score blocks are exchanged through LDS and summed, so both
+// waves of a pair hold identical scores and run the same softmax.
+// ---------------------------------------------------------------------------
+constexpr int kSplitWaves = 8;
+constexpr int kSplitThreads = kSplitWaves * 64;
+constexpr int kRingS = 3;                               // tiles resident in LDS
+constexpr int kHalfKSteps = kKSteps / 2;                // 18 k-steps per wave
+constexpr int kHalfDvBlocks = kDvBlocks / 2;            // 8 value blocks per wave
+constexpr int kXchgBytes = 64 * 16 * 4;                 // one wave's 32x32 fp32 score block
+constexpr int kRegKSteps = 16;                          // query k-steps held in VGPRs
+constexpr int kLdsKSteps = kHalfKSteps - kRegKSteps;    // the rest are re-read from LDS
+constexpr int kQParkBytes = kLdsKSteps * 64 * 16;       // per wave
+constexpr int kSplitLds = kRingS * kTileBytes + kSplitWaves * (kXchgBytes + kQParkBytes);  // 159744
+
+__global__ void __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+split_kernel(SplitArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSplitLds];
+  LDS_AS char* lds = lds_cast(smem);
+  LDS_AS char* xchg = lds + kRingS * kTileBytes;
+  LDS_AS char* qpark = xchg + kSplitWaves * kXchgBytes;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n = lane & 31;   // row of this lane within the pair's 32 rows
+  const int h = lane >> 5;   // k-half of the MFMA operands
+  const int pair = wave >> 1;
+  const int p = wave & 1;
+
+  // Workgroup -> (chunk, row tile). Consecutive ids go round-robin to the 8
+  // XCDs, so all row tiles of one chunk share an XCD and its L2.
+  const int wg = blockIdx.x;
+  const int xcd = wg & 7;
+  const int y = wg >> 3;
+  const int rt = y % a.row_tiles;
+  const int c = (y / a.row_tiles) * 8 + xcd;
+  if (c >= a.chunk_off[a.B]) return;
+  int lo = 0, hi = a.B;  // chunk_off[lo] <= c < chunk_off[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a.chunk_off[mid] <= c) lo = mid; else hi = mid;
+  }
+  const int b = lo;
+  int64_t P = a.prefix_lens[b];
+  P = P < 0 ? 0 : (P > a.total_kv ? a.total_kv : P);
+  const int64_t N = P + a.Q;
+  const int64_t sbase = a.seq_off[b];
+  const int64_t clen = a.chunk_len[b];
+  const int64_t kstart = (int64_t)(c - a.chunk_off[b]) * clen;
+  int64_t kend = kstart + clen;
+  if (kend > N) kend = N;
+  if (kend > a.total_kv - sbase) kend = a.total_kv - sbase;  // positions past the array are absent
+  const int nunits = kend > kstart ? (int)((kend - kstart + kUnit - 1) / kUnit) : 0;
+
+  // This lane's query-head row and its query position's tail-visibility bits.
+  const int r = rt * kRowsPerWG + pair * kRowsPerWave + n;
+  const bool row_ok = r < a.R;
+  const int rr = row_ok ? r : 0;
+  const int qi = rr / a.H;
+  uint64_t tbits = ~0ull;
+  if (row_ok) {
+    tbits = 0;
+    const uint8_t* mrow = a.tree_mask + ((int64_t)b * a.Q + qi) * a.Q;
+    for (int t = 0; t < a.Q; ++t) tbits |= (uint64_t)(mrow[t] != 0) << t;
+  }
+
+  // Resident queries: for k-step ks of this wave's dim half, lane (n + 32h)
+  // holds dims 288p + 16ks + 8h .. +7 of row n (zeros for padding rows). The
+  // last kLdsKSteps k-steps are parked in LDS to stay within 256 VGPRs.
+  bf16x8 qf[kRegKSteps];
+  LDS_AS char* my_q = qpark + wave * kQParkBytes + lane * 16;
+  {
+    const u32x4* qrow = reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * a.R + rr) * kLatent) +
+                        p * (kHalfKSteps * 2) + h;
+#pragma unroll
+    for (int ks = 0; ks < kHalfKSteps; ++ks) {
+      const u32x4 v = qrow[2 * ks];
+      const u32x4 vz = row_ok ? v : u32x4{0, 0, 0, 0};
+      if (ks < kRegKSteps) qf[ks] = __builtin_bit_cast(bf16x8, vz);
+      else *reinterpret_cast<LDS_AS u32x4*>(my_q + (ks - kRegKSteps) * 1024) = vz;
+    }
+  }
+
+  // Lane-constant LDS offsets.
+  // Score A operand: A-row n holds key swap_bits23(n), so that the score
+  // accumulator element i of lane (n + 32h) is key 16*(i/8) + 8h + (i%8).
+  const int arow_key = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
+  const int a_off = tile_offset(h, arow_key) + p * kHalfKSteps * 1024;   // + ks * 1024
+  // Value transpose reads: group g = lane/16, s = lane%16 supplies the address
+  // of V[key 16t + 8h + 4hf + s/4][dv 32db + 16(g%2) + 4(s%4) .. +3].
+  const int g = lane >> 4, s = lane & 15;
+  const int vchunk = 2 * (g & 1) + ((s & 3) >> 1);
+  const int tr_off0 = tile_offset(vchunk, 8 * h + (s >> 2)) + (s & 1) * 8 + p * kHalfDvBlocks * 2048;
+  const int tr_off1 = tile_offset(vchunk, 8 * h + 4 + (s >> 2)) + (s & 1) * 8 + p * kHalfDvBlocks * 2048;
+  LDS_AS char* my_x = xchg + wave * kXchgBytes + lane * 64;
+  LDS_AS char* even_x = xchg + (wave & ~1) * kXchgBytes + lane * 64;
+
+  // Gather bookkeeping: 36 wave-wide 1 KiB loads per tile; waves 0-3 issue 5,
+  // waves 4-7 issue 4. Lane l always fetches key gather_key(l) of a tile.
+  const int gkey = gather_key(lane);
+  const int ld_first = wave < 4 ? wave * 5 : 20 + (wave - 4) * 4;
+  const int ld_count = wave < 4 ? 5 : 4;
+  // Slot indices are loaded with inline assembly so that the compiler does
+  // not wait for them (with a vmcnt(0) that would drain the gathers); the
+  // loop's own vmcnt wait makes them valid, and the value is tied to that wait.
+  auto tile_key_ok = [&](int v) -> bool { return kstart + (int64_t)v * kUnit + gkey < kend; };
+  auto load_slot = [&](int v) -> int32_t {
+    const int64_t pos = kstart + (int64_t)v * kUnit + gkey;
+    const int32_t* ptr = a.kv_indices + (pos < kend ? sbase + pos : 0);
+    int32_t raw;
+    asm volatile("global_load_dword %0, %1, off" : "=v"(raw) : "v"(ptr) : "memory");
+    return raw;
+  };
+  auto issue = [&](int32_t slot, LDS_AS char* tile) {
+    const char* row = (slot >= 0 && slot < a.num_slots) ? a.kv_pool + (int64_t)slot * kRowBytes
+                                                        : reinterpret_cast<const char*>(g_zero_row);
+    row += h * 16;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      if (i < ld_count) {
+        const int ld = ld_first + i;
+        __builtin_amdgcn_global_load_lds(row + ld * 32, tile + ld * 1024, 16, 0, 0);
+      }
+    }
+  };
+
+  // Online-softmax state (log2 domain) and the output accumulators O^T.
+  float m_ref = -INFINITY;
+  float l_sum = 0.f;  // partial: this lane's half of the keys
+  f32x16 o[kHalfDvBlocks];
+#pragma unroll
+  for (int db = 0; db < kHalfDvBlocks; ++db) o[db] = f32x16{};
+
+  // Prologue, in the same order as the loop body: [slot u+3][tile u+2].
+  int32_t raw0 = load_slot(0);
+  int32_t raw1 = load_slot(1);
+  asm volatile("s_waitcnt vmcnt(0)" : "+v"(raw0), "+v"(raw1)::"memory");
+  issue(tile_key_ok(0) ? raw0 : -1, lds);
+  int32_t raw_next = load_slot(2);
+  issue(tile_key_ok(1) ? raw1 : -1, lds + kTileBytes);
+
+  for (int u = 0; u < nunits; ++u) {
+    // Since tile u went out, this wave issued one slot load and the 4 or 5
+    // loads of tile u+1. Once no more than those gathers are outstanding,
+    // tile u and the slot of tile u+2 have landed. The barrier is issued by
+    // hand so that it does not also drain the next tile's loads.
+    if (wave < 4) asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" : "+v"(raw_next)::"memory");
+    else asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" : "+v"(raw_next)::"memory");
+
+    LDS_AS char* tile = lds + (u % kRingS) * kTileBytes;
+    const int32_t slot_u2 = tile_key_ok(u + 2) ? raw_next : -1;
+    raw_next = load_slot(u + 3);
+    issue(slot_u2, lds + ((u + 2) % kRingS) * kTileBytes);  // tile u-1's slot is free
+
+    // ---- partial scores S^T over this wave's 288 dims
+    f32x16 sa = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < kHalfKSteps; ++ks) {
+      const bf16x8 k0 = *reinterpret_cast<LDS_AS const bf16x8*>(tile + a_off + ks * 1024);
+      const bf16x8 qv = ks < kRegKSteps
+                            ? qf[ks < kRegKSteps ? ks : 0]
+                            : *reinterpret_cast<LDS_AS const bf16x8*>(my_q + (ks - kRegKSteps) * 1024);
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qv, sa, 0, 0, 0);
+    }
+    // Exchange partial sums with the mate wave: both write their block, then
+    // both read the two blocks back and add them in the same order (even
+    // wave's half first), so the mates hold bitwise-identical scores.
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      *reinterpret_cast<LDS_AS f32x4*>(my_x + 16 * k) = f32x4{sa[4 * k], sa[4 * k + 1], sa[4 * k + 2], sa[4 * k + 3]};
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    float x[16];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f32x4 e = *reinterpret_cast<LDS_AS const f32x4*>(even_x + 16 * k);
+      const f32x4 d = *reinterpret_cast<LDS_AS const f32x4*>(even_x + kXchgBytes + 16 * k);
+      x[4 * k] = (e[0] + d[0]) * a.c_log2;
+      x[4 * k + 1] = (e[1] + d[1]) * a.c_log2;
+      x[4 * k + 2] = (e[2] + d[2]) * a.c_log2;
+      x[4 * k + 3] = (e[3] + d[3]) * a.c_log2;
+    }
+
+    // ---- mask, running max, lazy rescale, probabilities
+    const int64_t ustart = kstart + (int64_t)u * kUnit;
+    if (ustart + kUnit > P || ustart + kUnit > kend) {
+      // Branch-free selects: a short-circuit form of this test was compiled
+      // into control flow that dropped the -inf store for hidden tail keys.
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int64_t pos = ustart + 16 * (i >> 3) + 8 * h + (i & 7);
+        const int64_t rel = pos - P;
+        const unsigned tail_bit = (unsigned)(tbits >> (unsigned)(rel & 63)) & 1u;
+        const unsigned vis = (unsigned)(pos < kend) & ((unsigned)(rel < 0) | tail_bit);
+        x[i] = vis ? x[i] : -INFINITY;
+      }
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+    mx = fmaxf(mx, swap_halves(mx));
+    const bool grow = mx > m_ref + kLazyRescale;  // false while the row has seen nothing
+    if (__ballot(grow)) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.f;  // exp2(-inf) = 0
+      if (grow) m_ref = mx;
+      l_sum *= alpha;
+#pragma unroll
+      for (int db = 0; db < kHalfDvBlocks; ++db) o[db] *= alpha;
+    }
+    const float mref_safe = m_ref == -INFINITY ? 0.f : m_ref;
+    f16x8 p0, p1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float e0 = __builtin_amdgcn_exp2f(x[j] - mref_safe);
+      const float e1 = __builtin_amdgcn_exp2f(x[8 + j] - mref_safe);
+      l_sum += e0 + e1;
+      p0[j] = (_Float16)e0;
+      p1[j] = (_Float16)e1;
+    }
+
+    // ---- O^T += V^T P^T over this wave's 8 value blocks, two 16-key steps
+    // each. The four transpose reads of block db+1 are in flight while block
+    // db is converted and multiplied (lgkmcnt(4) leaves exactly them pending:
+    // nothing else touches LDS or the scalar cache in this stretch).
+    {
+      const unsigned tb0 = (unsigned)(uintptr_t)(tile + tr_off0);
+      const unsigned tb1 = (unsigned)(uintptr_t)(tile + tr_off1);
+      u32x2 cur[4], nxt[4];
+      cur[0] = tr16_read<0>(tb0);
+      cur[1] = tr16_read<0>(tb1);
+      cur[2] = tr16_read<256>(tb0);
+      cur[3] = tr16_read<256>(tb1);
+      static_for<0, kHalfDvBlocks>([&](auto dbc) {
+        constexpr int db = decltype(dbc)::value;
+        if constexpr (db + 1 < kHalfDvBlocks) {
+          nxt[0] = tr16_read<(db + 1) * 2048>(tb0);
+          nxt[1] = tr16_read<(db + 1) * 2048>(tb1);
+          nxt[2] = tr16_read<(db + 1) * 2048 + 256>(tb0);
+          nxt[3] = tr16_read<(db + 1) * 2048 + 256>(tb1);
+          // the wait is tied to the registers it makes valid, so the compiler
+          // cannot read them before it
+          asm volatile("s_waitcnt lgkmcnt(4)"
+                       : "+v"(cur[0]), "+v"(cur[1]), "+v"(cur[2]), "+v"(cur[3])::"memory");
+        } else {
+          asm volatile("s_waitcnt lgkmcnt(0)"
+                       : "+v"(cur[0]), "+v"(cur[1]), "+v"(cur[2]), "+v"(cur[3])::"memory");
+        }
+        f16x8 va0, va1;
+        bf16x4_to_f16(cur[0], va0, 0);
+        bf16x4_to_f16(cur[1], va0, 4);
+        bf16x4_to_f16(cur[2], va1, 0);
+        bf16x4_to_f16(cur[3], va1, 4);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va0, p0, o[db], 0, 0, 0);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va1, p1, o[db], 0, 0, 0);
+        if constexpr (db + 1 < kHalfDvBlocks) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) cur[k] = nxt[k];
+        }
+      });
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain prefetches before exit
+
+  // ---- epilogue: normalised partial and its lse (both waves agree on them)
+  const float l_tot = l_sum + swap_halves(l_sum);
+  const bool live = l_tot > 0.f;
+  const float inv = live ? 1.f / l_tot : 0.f;
+  const float lse_v = live ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+  if (row_ok) {
+    float* orow = a.part_o + ((int64_t)c * a.R + r) * kValue + p * (kValue / 2);
+#pragma unroll
+    for (int db = 0; db < kHalfDvBlocks; ++db) {
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const f32x4 v = {o[db][4 * qd] * inv, o[db][4 * qd + 1] * inv, o[db][4 * qd + 2] * inv,
+                         o[db][4 * qd + 3] * inv};
+        *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * qd + 4 * h) = v;
+      }
+    }
+    if (h == 0 && p == 0) a.part_lse[(int64_t)c * a.R + r] = lse_v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge: lse = ln sum_s exp(lse_s); out = sum_s exp(lse_s - lse) O_s.
+// Two rows per 256-thread workgroup, 4 value dims per thread.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) merge_kernel(const float* __restrict__ part_o,
+                                                    const float* __restrict__ part_lse,
+                                                    const int32_t* __restrict__ chunk_off,
+                                                    float* __restrict__ out, float* __restrict__ lse,
+                                                    int B, int R) {
+  const int64_t grow = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
+  if (grow >= (int64_t)B * R) return;
+  const int b = (int)(grow / R);
+  const int r = (int)(grow - (int64_t)b * R);
+  const int t = threadIdx.x & 127;
+  const int c0 = chunk_off[b], c1 = chunk_off[b + 1];
+  float mx = -INFINITY;
+  for (int c = c0; c < c1; ++c) mx = fmaxf(mx, part_lse[(int64_t)c * R + r]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float lse_v = -INFINITY;
+  if (mx > -INFINITY) {
+    float wsum = 0.f;
+    for (int c = c0; c < c1; ++c) {
+      const float w = __builtin_amdgcn_exp2f((part_lse[(int64_t)c * R + r] - mx) * kLog2e);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(part_o + ((int64_t)c * R + r) * kValue + 4 * t);
+      acc += w * v;
+      wsum += w;
+    }
+    acc *= 1.f / wsum;
+    lse_v = mx + __builtin_amdgcn_logf(wsum) * kLn2;
+  }
+  *reinterpret_cast<f32x4*>(out + grow * kValue + 4 * t) = acc;
+  if (t == 0) lse[grow] = lse_v;
+}
+
+// ---------------------------------------------------------------------------
+// Debug gather: the split kernel's gather routine, copied back out in order.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) debug_gather_kernel(const char* __restrict__ kv_pool,
+                                                           const int32_t* __restrict__ kv_indices,
+                                                           int64_t n, int64_t num_slots,
+                                                           u32x4* __restrict__ rows_out) {
+  __shared__ __attribute__((aligned(1024))) char smem[kTileBytes];
+  LDS_AS char* lds = lds_cast(smem);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t ustart = (int64_t)blockIdx.x * kUnit;
+  const int64_t pos = ustart + gather_key(lane);
+  const int64_t slot = pos < n ? (int64_t)kv_indices[pos] : -1;
+  issue_tile_gather(kv_pool, num_slots, slot, lds, wave, lane);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int p = tid; p < kUnit * kChunks; p += 256) {
+    const int key = p / kChunks, ch = p - key * kChunks;
+    if (ustart + key < n)
+      rows_out[(ustart + key) * kChunks + ch] =
+          *reinterpret_cast<LDS_AS const u32x4*>(lds + tile_offset(ch, key));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_plan(const int32_t* prefix_lens, int64_t* seq_off, int32_t* chunk_off,
+                       int32_t* chunk_len, int B, int Q, int64_t total_kv, int ideal_keys,
+                       int max_chunks, hipStream_t stream) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, prefix_lens, seq_off, chunk_off,
+                     chunk_len, B, Q, total_kv, ideal_keys, max_chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_split(const SplitArgs& a, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(split_kernel, dim3(grid), dim3(kSplitThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const float* part_o, const float* part_lse, const int32_t* chunk_off,
+                        float* out, float* lse, int B, int R, hipStream_t stream) {
+  const int64_t rows = (int64_t)B * R;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((rows + 1) / 2)), dim3(256), 0, stream, part_o,
+                     part_lse, chunk_off, out, lse, B, R);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_gather(const void* kv_pool, const int32_t* kv_indices, int64_t n,
+                               int64_t num_slots, void* rows_out, hipStream_t stream) {
+  const int64_t tiles = (n + kUnit - 1) / kUnit;
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(debug_gather_kernel, dim3((unsigned)tiles), dim3(256), 0, stream,
+                     static_cast<const char*>(kv_pool), kv_indices, n, num_slots,
+                     static_cast<u32x4*>(rows_out));
+  return hipGetLastError();
+}
+
+}  // namespace va

@@ -1,0 +1,99 @@
+"""CPU checks of the C ABI: the library loads, exports every declared entry point,
+and rejects bad arguments on the host before any launch (no GPU needed)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import speculative_decoding_verify_03_amd as va
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "verify_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(verify_attn\w*)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(va.LIB_PATH):
+        from speculative_decoding_verify_03_amd.build import build
+        build()
+    return va.load_library()
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(va.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_workspace_size_valid_and_invalid(lib):
+    assert lib.verify_attn_workspace_size(1, 16, 64, 185016) > 0
+    assert lib.verify_attn_workspace_size(0, 16, 64, 100) == 0      # B < 1
+    assert lib.verify_attn_workspace_size(1, 65, 8, 1000) == 0      # Q > 64
+    assert lib.verify_attn_workspace_size(2, 16, 8, 31) == 0        # total_kv < B*Q
+    assert lib.verify_attn_workspace_size(1, 4, 0, 100) == 0        # H < 1
+
+
+def _call(lib, **over):
+    args = dict(q=4096, kv=4096, idx=4096, pl=4096, tm=4096, scale=0.1, out=4096, lse=4096,
+                B=1, Q=4, H=8, slots=1024, total=260, ws=4096, wsb=1 << 40, stream=None)
+    args.update(over)
+    return lib.verify_attn(args["q"], args["kv"], args["idx"], args["pl"], args["tm"],
+                           args["scale"], args["out"], args["lse"], args["B"], args["Q"], args["H"],
+                           args["slots"], args["total"], args["ws"], args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), va.VA_EINVAL),
+    (dict(ws=None), va.VA_EINVAL),
+    (dict(q=4097), va.VA_EINVAL),           # misaligned
+    (dict(out=4104), va.VA_EINVAL),
+    (dict(lse=4098), va.VA_EINVAL),
+    (dict(ws=4096 + 128), va.VA_EINVAL),
+    (dict(B=0), va.VA_EINVAL),
+    (dict(Q=0), va.VA_EINVAL),
+    (dict(Q=65), va.VA_EINVAL),
+    (dict(H=0), va.VA_EINVAL),
+    (dict(total=3), va.VA_EINVAL),
+    (dict(slots=0), va.VA_EINVAL),
+    (dict(scale=float("nan")), va.VA_EINVAL),
+    (dict(wsb=16), va.VA_ENOSPC),
+])
+def test_bad_arguments_rejected_before_launch(lib, over, code):
+    assert _call(lib, **over) == code
+    assert lib.verify_attn_last_error().decode() != ""
+
+
+def test_debug_gather_argument_checks(lib):
+    assert lib.verify_attn_debug_gather(None, None, 0, 1, None, None) == va.VA_OK
+    assert lib.verify_attn_debug_gather(None, 4096, 5, 10, 4096, None) == va.VA_EINVAL
+    assert lib.verify_attn_debug_gather(4096, 4096, 5, 10, 4100, None) == va.VA_EINVAL
+    assert lib.verify_attn_debug_gather(4096, 4096, -1, 10, 4096, None) == va.VA_EINVAL
+
+
+def test_plan_shapes(lib):
+    va.set_chunk_override(0)
+    p = va.query_plan(1, 16, 64, 185016)
+    assert p["row_tiles"] == 8
+    assert p["chunk_keys"] % 32 == 0 and p["chunk_keys"] >= 256
+    assert p["grid"] % 8 == 0 and p["grid"] >= p["row_tiles"]
+    assert p["max_chunks"] >= (185016 + p["chunk_keys"] - 1) // p["chunk_keys"]
+    p1 = va.query_plan(1, 4, 8, 260)
+    assert p1["row_tiles"] == 1 and p1["chunk_keys"] == 256   # floor of 256 keys per chunk
+    va.set_chunk_override(64)
+    assert va.query_plan(1, 4, 8, 260)["chunk_keys"] == 64
+    va.set_chunk_override(0)
+    with pytest.raises(va.VerifyAttnError):
+        va.query_plan(1, 0, 8, 260)
