@@ -41,6 +41,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -185,37 +186,47 @@ __global__ void __launch_bounds__(256) plan_kernel(const int32_t* __restrict__ p
 // ---------------------------------------------------------------------------
 // Split kernel: one workgroup per (chunk, 128-row tile).
 //
-// 8 waves, two per SIMD. Waves 2j and 2j+1 form pair j and own the same 32
-// query-head rows; wave half p = wave & 1 computes the partial scores over
-// latent dims [288p, 288p + 288) and accumulates value dims [256p, 256p + 256).
-// The two partial score blocks are exchanged through LDS and summed, so both
-// waves of a pair hold identical scores and run the same softmax.
+// 8 waves, two per SIMD. Waves j and j+4 (same SIMD) form pair j and own
+// query-head rows [32j, 32j + 32) of the tile for the scores: wave half
+// p = wave / 4 computes the partial S^T over latent dims [288p, 288p + 288).
+// The odd half hands its partial block to the even half through LDS; the even
+// wave sums the two, runs the masked online softmax for the pair's 32 rows and
+// publishes P (fp16), the rescale factors and a rescale flag in LDS.
+// For the values every wave owns a 64-dim slice [64w, 64w + 64) of O^T for all
+// 128 rows, so each value element is transposed and converted only once per
+// workgroup and tile.
 // ---------------------------------------------------------------------------
 constexpr int kSplitWaves = 8;
 constexpr int kSplitThreads = kSplitWaves * 64;
 constexpr int kRingS = 3;                               // tiles resident in LDS
+constexpr int kPairs = 4;
 constexpr int kHalfKSteps = kKSteps / 2;                // 18 k-steps per wave
-constexpr int kHalfDvBlocks = kDvBlocks / 2;            // 8 value blocks per wave
-constexpr int kXchgBytes = 64 * 16 * 4;                 // one wave's 32x32 fp32 score block
+constexpr int kRowBlocks = kRowsPerWG / 32;             // 4 blocks of 32 rows
+constexpr int kWaveDvBlocks = kDvBlocks / kSplitWaves;  // 2 value blocks (64 dims) per wave
+constexpr int kXchgBytes = 64 * 16 * 4;                 // one 32x32 fp32 score block
+constexpr int kPBytes = 2 * 64 * 16;                    // one pair's P: two 16-key k-steps of f16x8
 constexpr int kRegKSteps = 16;                          // query k-steps held in VGPRs
 constexpr int kLdsKSteps = kHalfKSteps - kRegKSteps;    // the rest are re-read from LDS
 constexpr int kQParkBytes = kLdsKSteps * 64 * 16;       // per wave
-constexpr int kSplitLds = kRingS * kTileBytes + kSplitWaves * (kXchgBytes + kQParkBytes);  // 159744
+constexpr int kOffXchg = kRingS * kTileBytes;                      // 110592
+constexpr int kOffP = kOffXchg + kPairs * kXchgBytes;              // 126976
+constexpr int kOffAlpha = kOffP + kPairs * kPBytes;                // 135168
+constexpr int kOffFlag = kOffAlpha + kRowsPerWG * 4;               // 135680
+constexpr int kOffQPark = kOffFlag + 64;                           // 135744
+constexpr int kSplitLds = kOffQPark + kSplitWaves * kQParkBytes;   // 152128
 
 __global__ void __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 split_kernel(SplitArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem[kSplitLds];
   LDS_AS char* lds = lds_cast(smem);
-  LDS_AS char* xchg = lds + kRingS * kTileBytes;
-  LDS_AS char* qpark = xchg + kSplitWaves * kXchgBytes;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int n = lane & 31;   // row of this lane within the pair's 32 rows
+  const int n = lane & 31;   // row of this lane within a 32-row block
   const int h = lane >> 5;   // k-half of the MFMA operands
-  const int pair = wave >> 1;
-  const int p = wave & 1;
+  const int pair = wave & 3;
+  const int p = wave >> 2;   // 0: even half (softmax owner), 1: odd half
 
   // Workgroup -> (chunk, row tile). Consecutive ids go round-robin to the 8
   // XCDs, so all row tiles of one chunk share an XCD and its L2.
@@ -242,15 +253,14 @@ split_kernel(SplitArgs a) {
   if (kend > a.total_kv - sbase) kend = a.total_kv - sbase;  // positions past the array are absent
   const int nunits = kend > kstart ? (int)((kend - kstart + kUnit - 1) / kUnit) : 0;
 
-  // This lane's query-head row and its query position's tail-visibility bits.
-  const int r = rt * kRowsPerWG + pair * kRowsPerWave + n;
+  // Score rows of this lane (pair block) and its query's tail-visibility bits.
+  const int r = rt * kRowsPerWG + pair * 32 + n;
   const bool row_ok = r < a.R;
   const int rr = row_ok ? r : 0;
-  const int qi = rr / a.H;
   uint64_t tbits = ~0ull;
-  if (row_ok) {
+  if (row_ok && p == 0) {
     tbits = 0;
-    const uint8_t* mrow = a.tree_mask + ((int64_t)b * a.Q + qi) * a.Q;
+    const uint8_t* mrow = a.tree_mask + ((int64_t)b * a.Q + rr / a.H) * a.Q;
     for (int t = 0; t < a.Q; ++t) tbits |= (uint64_t)(mrow[t] != 0) << t;
   }
 
@@ -258,7 +268,7 @@ split_kernel(SplitArgs a) {
   // holds dims 288p + 16ks + 8h .. +7 of row n (zeros for padding rows). The
   // last kLdsKSteps k-steps are parked in LDS to stay within 256 VGPRs.
   bf16x8 qf[kRegKSteps];
-  LDS_AS char* my_q = qpark + wave * kQParkBytes + lane * 16;
+  LDS_AS char* my_q = lds + kOffQPark + wave * kQParkBytes + lane * 16;
   {
     const u32x4* qrow = reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * a.R + rr) * kLatent) +
                         p * (kHalfKSteps * 2) + h;
@@ -280,10 +290,12 @@ split_kernel(SplitArgs a) {
   // of V[key 16t + 8h + 4hf + s/4][dv 32db + 16(g%2) + 4(s%4) .. +3].
   const int g = lane >> 4, s = lane & 15;
   const int vchunk = 2 * (g & 1) + ((s & 3) >> 1);
-  const int tr_off0 = tile_offset(vchunk, 8 * h + (s >> 2)) + (s & 1) * 8 + p * kHalfDvBlocks * 2048;
-  const int tr_off1 = tile_offset(vchunk, 8 * h + 4 + (s >> 2)) + (s & 1) * 8 + p * kHalfDvBlocks * 2048;
-  LDS_AS char* my_x = xchg + wave * kXchgBytes + lane * 64;
-  LDS_AS char* even_x = xchg + (wave & ~1) * kXchgBytes + lane * 64;
+  const int tr_off0 = tile_offset(vchunk, 8 * h + (s >> 2)) + (s & 1) * 8 + wave * kWaveDvBlocks * 2048;
+  const int tr_off1 = tile_offset(vchunk, 8 * h + 4 + (s >> 2)) + (s & 1) * 8 + wave * kWaveDvBlocks * 2048;
+  LDS_AS char* xchg = lds + kOffXchg + pair * kXchgBytes + lane * 16;   // + k * 1024
+  LDS_AS char* pbuf = lds + kOffP + lane * 16;                          // + rb * kPBytes + t * 1024
+  LDS_AS char* abuf = lds + kOffAlpha;
+  LDS_AS char* fbuf = lds + kOffFlag;
 
   // Gather bookkeeping: 36 wave-wide 1 KiB loads per tile; waves 0-3 issue 5,
   // waves 4-7 issue 4. Lane l always fetches key gather_key(l) of a tile.
@@ -314,12 +326,15 @@ split_kernel(SplitArgs a) {
     }
   };
 
-  // Online-softmax state (log2 domain) and the output accumulators O^T.
+  // Online-softmax state of the pair's rows (log2 domain; kept by the even
+  // half) and this wave's output accumulators O^T: [row block][value block].
   float m_ref = -INFINITY;
   float l_sum = 0.f;  // partial: this lane's half of the keys
-  f32x16 o[kHalfDvBlocks];
+  f32x16 o[kRowBlocks][kWaveDvBlocks];
 #pragma unroll
-  for (int db = 0; db < kHalfDvBlocks; ++db) o[db] = f32x16{};
+  for (int rb = 0; rb < kRowBlocks; ++rb)
+#pragma unroll
+    for (int db = 0; db < kWaveDvBlocks; ++db) o[rb][db] = f32x16{};
 
   // Prologue, in the same order as the loop body: [slot u+3][tile u+2].
   int32_t raw0 = load_slot(0);
@@ -333,7 +348,9 @@ split_kernel(SplitArgs a) {
     // Since tile u went out, this wave issued one slot load and the 4 or 5
     // loads of tile u+1. Once no more than those gathers are outstanding,
     // tile u and the slot of tile u+2 have landed. The barrier is issued by
-    // hand so that it does not also drain the next tile's loads.
+    // hand so that it does not also drain the next tile's loads. It also
+    // guarantees that every wave is done with tile u-1 and with the P,
+    // rescale factors and flags of tile u-1.
     if (wave < 4) asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" : "+v"(raw_next)::"memory");
     else asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" : "+v"(raw_next)::"memory");
 
@@ -352,121 +369,147 @@ split_kernel(SplitArgs a) {
                             : *reinterpret_cast<LDS_AS const bf16x8*>(my_q + (ks - kRegKSteps) * 1024);
       sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qv, sa, 0, 0, 0);
     }
-    // Exchange partial sums with the mate wave: both write their block, then
-    // both read the two blocks back and add them in the same order (even
-    // wave's half first), so the mates hold bitwise-identical scores.
+    if (p == 1) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      *reinterpret_cast<LDS_AS f32x4*>(my_x + 16 * k) = f32x4{sa[4 * k], sa[4 * k + 1], sa[4 * k + 2], sa[4 * k + 3]};
+      for (int k = 0; k < 4; ++k)
+        *reinterpret_cast<LDS_AS f32x4*>(xchg + k * 1024) =
+            f32x4{sa[4 * k], sa[4 * k + 1], sa[4 * k + 2], sa[4 * k + 3]};
+    }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    float x[16];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const f32x4 e = *reinterpret_cast<LDS_AS const f32x4*>(even_x + 16 * k);
-      const f32x4 d = *reinterpret_cast<LDS_AS const f32x4*>(even_x + kXchgBytes + 16 * k);
-      x[4 * k] = (e[0] + d[0]) * a.c_log2;
-      x[4 * k + 1] = (e[1] + d[1]) * a.c_log2;
-      x[4 * k + 2] = (e[2] + d[2]) * a.c_log2;
-      x[4 * k + 3] = (e[3] + d[3]) * a.c_log2;
-    }
 
-    // ---- mask, running max, lazy rescale, probabilities
-    const int64_t ustart = kstart + (int64_t)u * kUnit;
-    if (ustart + kUnit > P || ustart + kUnit > kend) {
-      // Branch-free selects: a short-circuit form of this test was compiled
-      // into control flow that dropped the -inf store for hidden tail keys.
+    if (p == 0) {
+      // ---- full scores, mask, running max, lazy rescale, probabilities
+      float x[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int64_t pos = ustart + 16 * (i >> 3) + 8 * h + (i & 7);
-        const int64_t rel = pos - P;
-        const unsigned tail_bit = (unsigned)(tbits >> (unsigned)(rel & 63)) & 1u;
-        const unsigned vis = (unsigned)(pos < kend) & ((unsigned)(rel < 0) | tail_bit);
-        x[i] = vis ? x[i] : -INFINITY;
+      for (int k = 0; k < 4; ++k) {
+        const f32x4 d = *reinterpret_cast<LDS_AS const f32x4*>(xchg + k * 1024);
+        x[4 * k] = (sa[4 * k] + d[0]) * a.c_log2;
+        x[4 * k + 1] = (sa[4 * k + 1] + d[1]) * a.c_log2;
+        x[4 * k + 2] = (sa[4 * k + 2] + d[2]) * a.c_log2;
+        x[4 * k + 3] = (sa[4 * k + 3] + d[3]) * a.c_log2;
       }
-    }
-    float mx = x[0];
+      const int64_t ustart = kstart + (int64_t)u * kUnit;
+      if (ustart + kUnit > P || ustart + kUnit > kend) {
+        // Branch-free selects: a short-circuit form of this test was compiled
+        // into control flow that dropped the -inf store for hidden tail keys.
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
-    mx = fmaxf(mx, swap_halves(mx));
-    const bool grow = mx > m_ref + kLazyRescale;  // false while the row has seen nothing
-    if (__ballot(grow)) {
+        for (int i = 0; i < 16; ++i) {
+          const int64_t pos = ustart + 16 * (i >> 3) + 8 * h + (i & 7);
+          const int64_t rel = pos - P;
+          const unsigned tail_bit = (unsigned)(tbits >> (unsigned)(rel & 63)) & 1u;
+          const unsigned vis = (unsigned)(pos < kend) & ((unsigned)(rel < 0) | tail_bit);
+          x[i] = vis ? x[i] : -INFINITY;
+        }
+      }
+      float mx = x[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+      mx = fmaxf(mx, swap_halves(mx));
+      const bool grow = mx > m_ref + kLazyRescale;  // false while the row has seen nothing
       const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.f;  // exp2(-inf) = 0
       if (grow) m_ref = mx;
       l_sum *= alpha;
+      const float mref_safe = m_ref == -INFINITY ? 0.f : m_ref;
+      f16x8 p0, p1;
 #pragma unroll
-      for (int db = 0; db < kHalfDvBlocks; ++db) o[db] *= alpha;
-    }
-    const float mref_safe = m_ref == -INFINITY ? 0.f : m_ref;
-    f16x8 p0, p1;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float e0 = __builtin_amdgcn_exp2f(x[j] - mref_safe);
-      const float e1 = __builtin_amdgcn_exp2f(x[8 + j] - mref_safe);
-      l_sum += e0 + e1;
-      p0[j] = (_Float16)e0;
-      p1[j] = (_Float16)e1;
+      for (int j = 0; j < 8; ++j) {
+        const float e0 = __builtin_amdgcn_exp2f(x[j] - mref_safe);
+        const float e1 = __builtin_amdgcn_exp2f(x[8 + j] - mref_safe);
+        l_sum += e0 + e1;
+        p0[j] = (_Float16)e0;
+        p1[j] = (_Float16)e1;
+      }
+      *reinterpret_cast<LDS_AS f16x8*>(pbuf + pair * kPBytes) = p0;
+      *reinterpret_cast<LDS_AS f16x8*>(pbuf + pair * kPBytes + 1024) = p1;
+      const int any_grow = __ballot(grow) != 0;  // wave-wide: taken before any lane is masked off
+      if (h == 0) *reinterpret_cast<LDS_AS float*>(abuf + (pair * 32 + n) * 4) = alpha;
+      if (lane == 0) *reinterpret_cast<LDS_AS int*>(fbuf + pair * 4) = any_grow;
     }
 
-    // ---- O^T += V^T P^T over this wave's 8 value blocks, two 16-key steps
-    // each. The four transpose reads of block db+1 are in flight while block
-    // db is converted and multiplied (lgkmcnt(4) leaves exactly them pending:
-    // nothing else touches LDS or the scalar cache in this stretch).
+    // ---- this wave's value operands (independent of P): V^T for its two
+    // 32-dim blocks and both 16-key steps, transposed and converted to fp16
+    f16x8 va[kWaveDvBlocks][2];
     {
       const unsigned tb0 = (unsigned)(uintptr_t)(tile + tr_off0);
       const unsigned tb1 = (unsigned)(uintptr_t)(tile + tr_off1);
-      u32x2 cur[4], nxt[4];
-      cur[0] = tr16_read<0>(tb0);
-      cur[1] = tr16_read<0>(tb1);
-      cur[2] = tr16_read<256>(tb0);
-      cur[3] = tr16_read<256>(tb1);
-      static_for<0, kHalfDvBlocks>([&](auto dbc) {
-        constexpr int db = decltype(dbc)::value;
-        if constexpr (db + 1 < kHalfDvBlocks) {
-          nxt[0] = tr16_read<(db + 1) * 2048>(tb0);
-          nxt[1] = tr16_read<(db + 1) * 2048>(tb1);
-          nxt[2] = tr16_read<(db + 1) * 2048 + 256>(tb0);
-          nxt[3] = tr16_read<(db + 1) * 2048 + 256>(tb1);
-          // the wait is tied to the registers it makes valid, so the compiler
-          // cannot read them before it
-          asm volatile("s_waitcnt lgkmcnt(4)"
-                       : "+v"(cur[0]), "+v"(cur[1]), "+v"(cur[2]), "+v"(cur[3])::"memory");
-        } else {
-          asm volatile("s_waitcnt lgkmcnt(0)"
-                       : "+v"(cur[0]), "+v"(cur[1]), "+v"(cur[2]), "+v"(cur[3])::"memory");
-        }
-        f16x8 va0, va1;
-        bf16x4_to_f16(cur[0], va0, 0);
-        bf16x4_to_f16(cur[1], va0, 4);
-        bf16x4_to_f16(cur[2], va1, 0);
-        bf16x4_to_f16(cur[3], va1, 4);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va0, p0, o[db], 0, 0, 0);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va1, p1, o[db], 0, 0, 0);
-        if constexpr (db + 1 < kHalfDvBlocks) {
+      u32x2 v[kWaveDvBlocks][2][2];
+      v[0][0][0] = tr16_read<0>(tb0);
+      v[0][0][1] = tr16_read<0>(tb1);
+      v[0][1][0] = tr16_read<256>(tb0);
+      v[0][1][1] = tr16_read<256>(tb1);
+      v[1][0][0] = tr16_read<2048>(tb0);
+      v[1][0][1] = tr16_read<2048>(tb1);
+      v[1][1][0] = tr16_read<2048 + 256>(tb0);
+      v[1][1][1] = tr16_read<2048 + 256>(tb1);
+      // the wait is tied to the registers it makes valid, so the compiler
+      // cannot read them before it; lgkmcnt(0) also covers the P/alpha/flag
+      // stores of the even half before the barrier
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier"
+                   : "+v"(v[0][0][0]), "+v"(v[0][0][1]), "+v"(v[0][1][0]), "+v"(v[0][1][1]),
+                     "+v"(v[1][0][0]), "+v"(v[1][0][1]), "+v"(v[1][1][0]), "+v"(v[1][1][1])::"memory");
 #pragma unroll
-          for (int k = 0; k < 4; ++k) cur[k] = nxt[k];
+      for (int db = 0; db < kWaveDvBlocks; ++db)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          bf16x4_to_f16(v[db][t][0], va[db][t], 0);
+          bf16x4_to_f16(v[db][t][1], va[db][t], 4);
         }
-      });
+    }
+
+    // ---- rescale O for row blocks whose running max grew (rare)
+    const i32x4 flags = *reinterpret_cast<LDS_AS const i32x4*>(fbuf);
+    if (flags[0] | flags[1] | flags[2] | flags[3]) {
+#pragma unroll
+      for (int rb = 0; rb < kRowBlocks; ++rb) {
+        const float al = *reinterpret_cast<LDS_AS const float*>(abuf + (rb * 32 + n) * 4);
+#pragma unroll
+        for (int db = 0; db < kWaveDvBlocks; ++db) o[rb][db] *= al;
+      }
+    }
+
+    // ---- O^T += V^T P^T for this wave's 64 dims and all 128 rows
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb) {
+      const f16x8 pb0 = *reinterpret_cast<LDS_AS const f16x8*>(pbuf + rb * kPBytes);
+      const f16x8 pb1 = *reinterpret_cast<LDS_AS const f16x8*>(pbuf + rb * kPBytes + 1024);
+#pragma unroll
+      for (int db = 0; db < kWaveDvBlocks; ++db) {
+        o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[db][0], pb0, o[rb][db], 0, 0, 0);
+        o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[db][1], pb1, o[rb][db], 0, 0, 0);
+      }
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain prefetches before exit
 
-  // ---- epilogue: normalised partial and its lse (both waves agree on them)
-  const float l_tot = l_sum + swap_halves(l_sum);
-  const bool live = l_tot > 0.f;
-  const float inv = live ? 1.f / l_tot : 0.f;
-  const float lse_v = live ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-  if (row_ok) {
-    float* orow = a.part_o + ((int64_t)c * a.R + r) * kValue + p * (kValue / 2);
+  // ---- epilogue: the even halves publish 1/l per row (reusing the alpha
+  // slots) and write lse; every wave normalises and writes its 64 dims.
+  {
+    const float l_tot = l_sum + swap_halves(l_sum);
+    const bool live = l_tot > 0.f;
+    asm volatile("s_barrier" ::: "memory");  // all waves are past their last alpha read
+    if (p == 0) {
+      if (h == 0) *reinterpret_cast<LDS_AS float*>(abuf + (pair * 32 + n) * 4) = live ? 1.f / l_tot : 0.f;
+      const float lse_v = live ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+      if (row_ok && h == 0) a.part_lse[(int64_t)c * a.R + r] = lse_v;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-    for (int db = 0; db < kHalfDvBlocks; ++db) {
+    for (int rb = 0; rb < kRowBlocks; ++rb) {
+      const int rw = rt * kRowsPerWG + rb * 32 + n;
+      const float inv = *reinterpret_cast<LDS_AS const float*>(abuf + (rb * 32 + n) * 4);
+      if (rw < a.R) {
+        float* orow = a.part_o + ((int64_t)c * a.R + rw) * kValue + wave * kWaveDvBlocks * 32;
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const f32x4 v = {o[db][4 * qd] * inv, o[db][4 * qd + 1] * inv, o[db][4 * qd + 2] * inv,
-                         o[db][4 * qd + 3] * inv};
-        *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * qd + 4 * h) = v;
+        for (int db = 0; db < kWaveDvBlocks; ++db) {
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd) {
+            const f32x4 v = {o[rb][db][4 * qd] * inv, o[rb][db][4 * qd + 1] * inv,
+                             o[rb][db][4 * qd + 2] * inv, o[rb][db][4 * qd + 3] * inv};
+            *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * qd + 4 * h) = v;
+          }
+        }
       }
     }
-    if (h == 0 && p == 0) a.part_lse[(int64_t)c * a.R + r] = lse_v;
   }
 }
 

@@ -175,3 +175,24 @@ def test_debug_gather_bit_exact(env, n):
     got = rows.cpu().numpy().view(np.uint16)
     want = np.where(((idx >= 0) & (idx < 2048))[:, None], pool[np.clip(idx, 0, 2047)], 0).astype(np.uint16)
     assert np.array_equal(got, want)
+
+
+def test_late_max_growth_rescales_some_rows(env):
+    """Keys aligned with one query-head row late in the sequence make that row's
+    running max jump long after the first tile while its neighbours' maxima stay
+    put, so the lazy rescale has to act on a subset of rows only."""
+    torch, va = env
+    w = make_workload("growth", [307], B=1, Q=4, H=32, prefix_lens=[3000], mask="chain", num_slots=4096)
+    qrow = w.q[0, 1, 5].astype(np.uint32) << 16           # query position 1, head 5
+    qf = qrow.view(np.float32) * np.float32(0.25)
+    from workloads import bf16_from_f32
+    for pos in (1500, 2800, 2999):
+        w.kv_pool[w.kv_indices[pos]] = bf16_from_f32(qf)
+    qrow2 = w.q[0, 3, 30].astype(np.uint32) << 16         # another row grows in a different chunk
+    w.kv_pool[w.kv_indices[700]] = bf16_from_f32(qrow2.view(np.float32) * np.float32(0.2))
+    for chunk in (0, 1024):
+        va.set_chunk_override(chunk)
+        try:
+            _check(env, w, label=f"growth_chunk{chunk}")
+        finally:
+            va.set_chunk_override(0)
