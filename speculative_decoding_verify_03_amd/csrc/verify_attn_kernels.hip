@@ -7,26 +7,22 @@
 // chunk through LDS in 32-key tiles with an online softmax, and a second
 // kernel merges the chunk partials by log-sum-exp.
 //
-// gfx950 mapping, per workgroup (4 waves, one per SIMD, 128 query-head rows):
+// gfx950 mapping, per workgroup (8 waves, two per SIMD, 128 query-head rows):
 //  * gather: every 32-key tile is brought into LDS with 16-byte direct
-//    global->LDS loads through kv_indices (page_size 1, 1152-byte rows); a
-//    4-deep ring of tiles keeps three tiles in flight;
-//  * scores: S^T = K Q^T on MFMA 32x32x16 bf16. K comes from LDS (A operand),
-//    the wave's 32 query rows stay resident in VGPRs (B operand). All heads
-//    and verify positions of the tile share every latent row that is loaded;
-//  * softmax: each lane owns one row, so the running max / sum need only one
-//    cross-half exchange per tile; rescaling is lazy (only when a row max
-//    grows by more than 2^8);
-//  * values: O^T += V^T P^T on MFMA 32x32x16 fp16. P^T is taken straight
-//    from the score accumulators (no data movement), V^T is read from the same
-//    LDS tile with the gfx950 transpose read ds_read_b64_tr_b16 and converted
-//    bf16 -> fp16 in registers. P is fp16 (not bf16) for accuracy: fp16 keeps
-//    11 significant bits against bf16's 8.
-//
-// LDS tile layout (one 32-key tile, 36 KiB): 72 "chunk columns" of 16 bytes
-// (8 latent dims) x 32 key slots. Chunk c of key k sits at slot
-// (c * 32 + (k ^ 4 * (c & 1))) * 16; the xor keeps the transpose reads of V
-// at the 2-way minimum for 512-byte wave accesses.
+//    global->LDS loads through kv_indices (page_size 1, 1152-byte rows), one
+//    whole 128-byte line per 8 lanes; a 3-deep ring keeps two tiles in flight;
+//  * scores: S^T = K Q^T on MFMA 32x32x16 bf16. K comes from LDS (A operand);
+//    each pair of waves keeps its 32 query rows resident in VGPRs (B operand),
+//    split by latent dims. All heads and verify positions of the tile share
+//    every latent row that is loaded;
+//  * softmax: one wave per pair owns it; each lane owns one row, so the running
+//    max needs one cross-half exchange per tile; rescaling is lazy (only when
+//    a row max grows by more than 2^8);
+//  * values: O^T += V^T P^T on MFMA 32x32x16 fp16. P^T is the score
+//    accumulator layout itself (published through LDS), V^T is read from the
+//    same LDS tile with the gfx950 transpose read ds_read_b64_tr_b16 and
+//    converted bf16 -> fp16 in registers. P is fp16 (not bf16) for accuracy:
+//    fp16 keeps 11 significant bits against bf16's 8.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -50,7 +46,6 @@ constexpr int kTileBytes = kUnit * kRowBytes;    // 36864 bytes per tile
 constexpr int kRing = 4;                         // tiles resident in LDS
 constexpr int kKSteps = kLatent / 16;            // 36 MFMA k-steps over the latent
 constexpr int kDvBlocks = kValue / 32;           // 16 value blocks of 32 dims
-constexpr int kLoadsPerWave = kChunks / 2 / kWaves;  // 9 wave-wide 1 KiB loads per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyRescale = 8.0f;             // log2 headroom before O is rescaled
@@ -59,57 +54,56 @@ constexpr float kLazyRescale = 8.0f;             // log2 headroom before O is re
 // never holds anything but finite data and a masked key contributes 0 * 0.
 __device__ __attribute__((aligned(16))) uint32_t g_zero_row[kRowBytes / 4] = {0};
 
-// Byte offset of (chunk column, key) inside one LDS tile.
+// Byte offset of (16-byte chunk c, key k) inside one LDS tile. The tile is
+// 36 regions of 1 KiB, one per (group of 8 keys, 128-byte line of the row);
+// inside a region, key k%8 owns 8 slots and chunk c%8 sits at slot
+// (c%8) ^ ((k >> 1) & 7). The xor spreads both the score reads (32 keys, one
+// chunk) and the value transpose reads over all banks.
 __device__ __forceinline__ int tile_offset(int chunk, int key) {
-  return (chunk * kUnit + (key ^ ((chunk & 1) << 2))) * 16;
+  return ((key >> 3) * 9 + (chunk >> 3)) * 1024 + ((key & 7) * 8 + ((chunk & 7) ^ ((key >> 1) & 7))) * 16;
 }
 
-// Key that lane `lane` fetches for every 1 KiB load of a tile: load q of the
-// tile writes chunks 2q and 2q+1; lane l lands at slot (2q + l/32, l%32).
-__device__ __forceinline__ int gather_key(int lane) { return (lane & 31) ^ ((lane >> 5) << 2); }
+// The gather is line-granular: wave w of the 8 fetches key group w/2 (8 keys)
+// and 128-byte lines [0, 5) (even w) or [5, 9) (odd w) of each of those rows;
+// lane l reads key 8(w/2) + l/8 and the 16-byte chunk of the line that lands in
+// slot l of the region. Every load instruction thus fetches 8 whole lines.
+struct GatherLane {
+  int key;   // key of the tile this lane fetches
+  int coff;  // byte offset of its chunk inside a 128-byte line
+  int kg;    // key group (region row)
+  int L0;    // first line
+  int nld;   // number of lines (5 or 4)
+};
 
-// Issue this wave's share (9 x 1 KiB) of one tile gather. `slot` is the pool
-// row of gather_key(lane) (or any out-of-range value for an absent position).
-__device__ __forceinline__ void issue_tile_gather(const char* kv_pool, int64_t num_slots, int64_t slot,
-                                                  LDS_AS char* tile, int wave, int lane) {
-  const char* row = (slot >= 0 && slot < num_slots) ? kv_pool + slot * (int64_t)kRowBytes
+__device__ __forceinline__ GatherLane gather_lane(int wave, int lane) {
+  GatherLane g;
+  g.kg = wave >> 1;
+  g.key = 8 * g.kg + (lane >> 3);
+  g.coff = ((lane & 7) ^ ((g.key >> 1) & 7)) * 16;
+  g.L0 = (wave & 1) ? 5 : 0;
+  g.nld = (wave & 1) ? 4 : 5;
+  return g;
+}
+
+// Issue this wave's share of one tile gather. `slot` is the pool row of the
+// lane's key (any out-of-range value for an absent position: zero row).
+__device__ __forceinline__ void issue_tile_gather(const char* kv_pool, int64_t num_slots, int32_t slot,
+                                                  LDS_AS char* tile, const GatherLane& gl) {
+  const char* row = (slot >= 0 && slot < num_slots) ? kv_pool + (int64_t)slot * kRowBytes
                                                     : reinterpret_cast<const char*>(g_zero_row);
-  row += (lane >> 5) * 16;
+  row += gl.coff;
 #pragma unroll
-  for (int i = 0; i < kLoadsPerWave; ++i) {
-    const int ld = wave * kLoadsPerWave + i;
-    __builtin_amdgcn_global_load_lds(row + ld * 32, tile + ld * 1024, 16, 0, 0);
+  for (int i = 0; i < 5; ++i) {
+    if (i < gl.nld) {
+      const int L = gl.L0 + i;
+      __builtin_amdgcn_global_load_lds(row + L * 128, tile + (gl.kg * 9 + L) * 1024, 16, 0, 0);
+    }
   }
 }
 
 __device__ __forceinline__ LDS_AS char* lds_cast(char* p) { return (LDS_AS char*)(p); }
 
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
-template <int I>
-struct IntC {
-  static constexpr int value = I;
-};
-// Calls f(IntC<0>{}) ... f(IntC<N-1>{}): compile-time loop indices for code
-// that needs them as immediates (instruction offsets).
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(IntC<I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
-// ds_read_b64_tr_b16 issued as inline assembly. The compiler would otherwise
-// put a full vmcnt(0) in front of it (it cannot tell that the read does not
-// alias the direct-to-LDS loads still in flight), draining the gather
-// prefetch. The caller waits for the result with an explicit lgkmcnt.
-template <int kOffset>
-__device__ __forceinline__ u32x2 tr16_read(unsigned lds_addr) {
-  u32x2 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "i"(kOffset));
-  return r;
-}
 
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
 
@@ -212,8 +206,10 @@ constexpr int kOffXchg = kRingS * kTileBytes;                      // 110592
 constexpr int kOffP = kOffXchg + kPairs * kXchgBytes;              // 126976
 constexpr int kOffAlpha = kOffP + kPairs * kPBytes;                // 135168
 constexpr int kOffFlag = kOffAlpha + kRowsPerWG * 4;               // 135680
-constexpr int kOffQPark = kOffFlag + 64;                           // 135744
-constexpr int kSplitLds = kOffQPark + kSplitWaves * kQParkBytes;   // 152128
+constexpr int kOffSlots = kOffFlag + 64;                           // 135744: slot-index ring
+constexpr int kSlotRing = 3;                                       // 256 bytes per tile
+constexpr int kOffQPark = kOffSlots + kSlotRing * 256;             // 136512
+constexpr int kSplitLds = kOffQPark + kSplitWaves * kQParkBytes;   // 152896
 
 __global__ void __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 split_kernel(SplitArgs a) {
@@ -284,47 +280,57 @@ split_kernel(SplitArgs a) {
   // Lane-constant LDS offsets.
   // Score A operand: A-row n holds key swap_bits23(n), so that the score
   // accumulator element i of lane (n + 32h) is key 16*(i/8) + 8h + (i%8).
+  // Its k-step ks of this wave reads chunk 2(18p + ks) + h; a_off[j] is the
+  // address for ks = j, and ks = j + 4q adds q KiB.
   const int arow_key = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
-  const int a_off = tile_offset(h, arow_key) + p * kHalfKSteps * 1024;   // + ks * 1024
+  int a_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) a_off[j] = tile_offset(2 * (kHalfKSteps * p + j) + h, arow_key);
   // Value transpose reads: group g = lane/16, s = lane%16 supplies the address
-  // of V[key 16t + 8h + 4hf + s/4][dv 32db + 16(g%2) + 4(s%4) .. +3].
+  // of V[key 16t + 8h + 4hf + s/4][dv 32db + 16(g%2) + 4(s%4) .. +3] for this
+  // wave's blocks db = 2w + d; key 16t adds 18 KiB (t is an immediate).
   const int g = lane >> 4, s = lane & 15;
-  const int vchunk = 2 * (g & 1) + ((s & 3) >> 1);
-  const int tr_off0 = tile_offset(vchunk, 8 * h + (s >> 2)) + (s & 1) * 8 + wave * kWaveDvBlocks * 2048;
-  const int tr_off1 = tile_offset(vchunk, 8 * h + 4 + (s >> 2)) + (s & 1) * 8 + wave * kWaveDvBlocks * 2048;
+  int tr_off[2][2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+      tr_off[hf][d] = tile_offset(4 * (2 * wave + d) + 2 * (g & 1) + ((s & 3) >> 1), 8 * h + 4 * hf + (s >> 2)) +
+                      (s & 1) * 8;
   LDS_AS char* xchg = lds + kOffXchg + pair * kXchgBytes + lane * 16;   // + k * 1024
   LDS_AS char* pbuf = lds + kOffP + lane * 16;                          // + rb * kPBytes + t * 1024
   LDS_AS char* abuf = lds + kOffAlpha;
   LDS_AS char* fbuf = lds + kOffFlag;
 
-  // Gather bookkeeping: 36 wave-wide 1 KiB loads per tile; waves 0-3 issue 5,
-  // waves 4-7 issue 4. Lane l always fetches key gather_key(l) of a tile.
-  const int gkey = gather_key(lane);
-  const int ld_first = wave < 4 ? wave * 5 : 20 + (wave - 4) * 4;
-  const int ld_count = wave < 4 ? 5 : 4;
-  // Slot indices are loaded with inline assembly so that the compiler does
-  // not wait for them (with a vmcnt(0) that would drain the gathers); the
-  // loop's own vmcnt wait makes them valid, and the value is tied to that wait.
+  // Gather bookkeeping (see gather_lane): even waves issue 5 loads per tile,
+  // odd waves 4; lane l always fetches key gl.key of a tile.
+  const GatherLane gl = gather_lane(wave, lane);
+  const int gkey = gl.key;
+  // Slot indices travel through LDS like the latent rows: wave 0 copies the
+  // 32 kv_indices entries of tile v into ring entry v % 3 with one
+  // direct-to-LDS dword load (lanes 32-63 duplicate lanes 0-31), one tile
+  // before the gather that needs them, so the loop-top vmcnt wait covers them
+  // too. (A register load would make the compiler wait for it with a vmcnt
+  // that also drains the gathers issued after it.)
+  LDS_AS char* slot_ring = lds + kOffSlots;
   auto tile_key_ok = [&](int v) -> bool { return kstart + (int64_t)v * kUnit + gkey < kend; };
-  auto load_slot = [&](int v) -> int32_t {
-    const int64_t pos = kstart + (int64_t)v * kUnit + gkey;
-    const int32_t* ptr = a.kv_indices + (pos < kend ? sbase + pos : 0);
-    int32_t raw;
-    asm volatile("global_load_dword %0, %1, off" : "=v"(raw) : "v"(ptr) : "memory");
-    return raw;
-  };
-  auto issue = [&](int32_t slot, LDS_AS char* tile) {
-    const char* row = (slot >= 0 && slot < a.num_slots) ? a.kv_pool + (int64_t)slot * kRowBytes
-                                                        : reinterpret_cast<const char*>(g_zero_row);
-    row += h * 16;
-#pragma unroll
-    for (int i = 0; i < 5; ++i) {
-      if (i < ld_count) {
-        const int ld = ld_first + i;
-        __builtin_amdgcn_global_load_lds(row + ld * 32, tile + ld * 1024, 16, 0, 0);
-      }
+  auto load_slots_to_lds = [&](int v) {
+    if (wave == 0) {
+      int64_t gpos = sbase + kstart + (int64_t)v * kUnit + (lane & 31);
+      gpos = gpos < a.total_kv ? gpos : a.total_kv - 1;
+      gpos = gpos < 0 ? 0 : gpos;
+      __builtin_amdgcn_global_load_lds(a.kv_indices + gpos, slot_ring + (v % kSlotRing) * 256, 4, 0, 0);
     }
   };
+  auto read_slot = [&](int v) -> int32_t {
+    const int32_t sl = *reinterpret_cast<LDS_AS const int32_t*>(slot_ring + (v % kSlotRing) * 256 + gkey * 4);
+    return tile_key_ok(v) ? sl : -1;
+  };
+  auto load_slot = [&](int v) -> int32_t {
+    const int64_t pos = kstart + (int64_t)v * kUnit + gkey;
+    return pos < kend ? a.kv_indices[sbase + pos] : -1;
+  };
+  auto issue = [&](int32_t slot, LDS_AS char* tile) { issue_tile_gather(a.kv_pool, a.num_slots, slot, tile, gl); };
 
   // Online-softmax state of the pair's rows (log2 domain; kept by the even
   // half) and this wave's output accumulators O^T: [row block][value block].
@@ -336,34 +342,37 @@ split_kernel(SplitArgs a) {
 #pragma unroll
     for (int db = 0; db < kWaveDvBlocks; ++db) o[rb][db] = f32x16{};
 
-  // Prologue, in the same order as the loop body: [slot u+3][tile u+2].
-  int32_t raw0 = load_slot(0);
-  int32_t raw1 = load_slot(1);
-  asm volatile("s_waitcnt vmcnt(0)" : "+v"(raw0), "+v"(raw1)::"memory");
-  issue(tile_key_ok(0) ? raw0 : -1, lds);
-  int32_t raw_next = load_slot(2);
-  issue(tile_key_ok(1) ? raw1 : -1, lds + kTileBytes);
+  // Prologue, in the same order as the loop body: [slots u+3][tile u+2].
+  {
+    const int32_t s0 = load_slot(0);
+    const int32_t s1 = load_slot(1);
+    issue(s0, lds);
+    load_slots_to_lds(2);
+    issue(s1, lds + kTileBytes);
+  }
 
   for (int u = 0; u < nunits; ++u) {
-    // Since tile u went out, this wave issued one slot load and the 4 or 5
-    // loads of tile u+1. Once no more than those gathers are outstanding,
-    // tile u and the slot of tile u+2 have landed. The barrier is issued by
-    // hand so that it does not also drain the next tile's loads. It also
+    // Since tile u went out, this wave issued the 5 or 4 loads of tile u+1
+    // (wave 0 also the slot copy of tile u+2, before them). Once no more than
+    // those gathers are outstanding, tile u and the slots of tile u+2 have
+    // landed (the compiler does not track direct-to-LDS loads, so this wait
+    // is explicit). The barrier is issued by hand so that it does
+    // not also drain the next tile's loads. It also
     // guarantees that every wave is done with tile u-1 and with the P,
     // rescale factors and flags of tile u-1.
-    if (wave < 4) asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" : "+v"(raw_next)::"memory");
-    else asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" : "+v"(raw_next)::"memory");
+    if ((wave & 1) == 0) asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
 
     LDS_AS char* tile = lds + (u % kRingS) * kTileBytes;
-    const int32_t slot_u2 = tile_key_ok(u + 2) ? raw_next : -1;
-    raw_next = load_slot(u + 3);
+    const int32_t slot_u2 = read_slot(u + 2);
+    load_slots_to_lds(u + 3);
     issue(slot_u2, lds + ((u + 2) % kRingS) * kTileBytes);  // tile u-1's slot is free
 
     // ---- partial scores S^T over this wave's 288 dims
     f32x16 sa = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < kHalfKSteps; ++ks) {
-      const bf16x8 k0 = *reinterpret_cast<LDS_AS const bf16x8*>(tile + a_off + ks * 1024);
+      const bf16x8 k0 = *reinterpret_cast<LDS_AS const bf16x8*>(tile + a_off[ks & 3] + (ks >> 2) * 1024);
       const bf16x8 qv = ks < kRegKSteps
                             ? qf[ks < kRegKSteps ? ks : 0]
                             : *reinterpret_cast<LDS_AS const bf16x8*>(my_q + (ks - kRegKSteps) * 1024);
@@ -430,23 +439,36 @@ split_kernel(SplitArgs a) {
     // 32-dim blocks and both 16-key steps, transposed and converted to fp16
     f16x8 va[kWaveDvBlocks][2];
     {
-      const unsigned tb0 = (unsigned)(uintptr_t)(tile + tr_off0);
-      const unsigned tb1 = (unsigned)(uintptr_t)(tile + tr_off1);
-      u32x2 v[kWaveDvBlocks][2][2];
-      v[0][0][0] = tr16_read<0>(tb0);
-      v[0][0][1] = tr16_read<0>(tb1);
-      v[0][1][0] = tr16_read<256>(tb0);
-      v[0][1][1] = tr16_read<256>(tb1);
-      v[1][0][0] = tr16_read<2048>(tb0);
-      v[1][0][1] = tr16_read<2048>(tb1);
-      v[1][1][0] = tr16_read<2048 + 256>(tb0);
-      v[1][1][1] = tr16_read<2048 + 256>(tb1);
-      // the wait is tied to the registers it makes valid, so the compiler
-      // cannot read them before it; lgkmcnt(0) also covers the P/alpha/flag
-      // stores of the even half before the barrier
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier"
-                   : "+v"(v[0][0][0]), "+v"(v[0][0][1]), "+v"(v[0][1][0]), "+v"(v[0][1][1]),
-                     "+v"(v[1][0][0]), "+v"(v[1][0][1]), "+v"(v[1][1][0]), "+v"(v[1][1][1])::"memory");
+      // The eight transpose reads and their wait form one asm statement, so the
+      // outputs are complete when it ends. (As separate builtins the compiler
+      // fences each with vmcnt(0) against the direct-to-LDS loads in flight,
+      // which would drain the gather prefetch; split into an asm read plus a
+      // later wait, the compiler may copy a destination register before the
+      // data has arrived.)
+      u32x2 v[kWaveDvBlocks][2][2];   // [d][t][hf]
+      {
+        const unsigned a00 = (unsigned)(uintptr_t)(tile + tr_off[0][0]);
+        const unsigned a10 = (unsigned)(uintptr_t)(tile + tr_off[1][0]);
+        const unsigned a01 = (unsigned)(uintptr_t)(tile + tr_off[0][1]);
+        const unsigned a11 = (unsigned)(uintptr_t)(tile + tr_off[1][1]);
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %8\n\t"
+            "ds_read_b64_tr_b16 %1, %9\n\t"
+            "ds_read_b64_tr_b16 %2, %8 offset:18432\n\t"
+            "ds_read_b64_tr_b16 %3, %9 offset:18432\n\t"
+            "ds_read_b64_tr_b16 %4, %10\n\t"
+            "ds_read_b64_tr_b16 %5, %11\n\t"
+            "ds_read_b64_tr_b16 %6, %10 offset:18432\n\t"
+            "ds_read_b64_tr_b16 %7, %11 offset:18432\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(v[0][0][0]), "=&v"(v[0][0][1]), "=&v"(v[0][1][0]), "=&v"(v[0][1][1]),
+              "=&v"(v[1][0][0]), "=&v"(v[1][0][1]), "=&v"(v[1][1][0]), "=&v"(v[1][1][1])
+            : "v"(a00), "v"(a10), "v"(a01), "v"(a11)
+            : "memory");
+      }
+      // all LDS stores of this iteration (P/alpha/flag of the even half) are
+      // complete before the barrier
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
       for (int db = 0; db < kWaveDvBlocks; ++db)
 #pragma unroll
@@ -550,20 +572,22 @@ __global__ void __launch_bounds__(256) merge_kernel(const float* __restrict__ pa
 // ---------------------------------------------------------------------------
 // Debug gather: the split kernel's gather routine, copied back out in order.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) debug_gather_kernel(const char* __restrict__ kv_pool,
+__global__ void __launch_bounds__(512) debug_gather_kernel(const char* __restrict__ kv_pool,
                                                            const int32_t* __restrict__ kv_indices,
                                                            int64_t n, int64_t num_slots,
                                                            u32x4* __restrict__ rows_out) {
   __shared__ __attribute__((aligned(1024))) char smem[kTileBytes];
   LDS_AS char* lds = lds_cast(smem);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const GatherLane gl = gather_lane(wave, lane);
   const int64_t ustart = (int64_t)blockIdx.x * kUnit;
-  const int64_t pos = ustart + gather_key(lane);
-  const int64_t slot = pos < n ? (int64_t)kv_indices[pos] : -1;
-  issue_tile_gather(kv_pool, num_slots, slot, lds, wave, lane);
+  const int64_t pos = ustart + gl.key;
+  const int32_t slot = pos < n ? kv_indices[pos] : -1;
+  issue_tile_gather(kv_pool, num_slots, slot, lds, gl);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int p = tid; p < kUnit * kChunks; p += 256) {
+  for (int p = tid; p < kUnit * kChunks; p += 512) {
     const int key = p / kChunks, ch = p - key * kChunks;
     if (ustart + key < n)
       rows_out[(ustart + key) * kChunks + ch] =
@@ -599,7 +623,7 @@ hipError_t launch_debug_gather(const void* kv_pool, const int32_t* kv_indices, i
                                int64_t num_slots, void* rows_out, hipStream_t stream) {
   const int64_t tiles = (n + kUnit - 1) / kUnit;
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(debug_gather_kernel, dim3((unsigned)tiles), dim3(256), 0, stream,
+  hipLaunchKernelGGL(debug_gather_kernel, dim3((unsigned)tiles), dim3(512), 0, stream,
                      static_cast<const char*>(kv_pool), kv_indices, n, num_slots,
                      static_cast<u32x4*>(rows_out));
   return hipGetLastError();
