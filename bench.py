@@ -67,8 +67,15 @@ def visible_pairs(w) -> int:
 
 
 def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Digest of the kernel source with comments and blank lines removed, so that the
+    committed counter summary stays tied to the code it was taken on."""
+    import re
+    with open(KERNEL_SRC) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [ln.split("//", 1)[0].rstrip() for ln in text.splitlines()]
+    code = "\n".join(ln for ln in lines if ln.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def measured_traffic():
@@ -84,8 +91,9 @@ def measured_traffic():
     return s.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(w, heads, reps=1):
-    """The fp64 oracle (as is) on a head subset of the same workload, scaled to one call."""
+def cpu_baseline(w, heads, min_seconds=10.0, max_reps=20):
+    """The fp64 oracle (as is) on the same workload, repeated until at least
+    `min_seconds` of CPU work have run, reported per call."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -93,10 +101,13 @@ def cpu_baseline(w, heads, reps=1):
     except Exception:  # pragma: no cover
         blas_threads = None
     t0 = time.perf_counter()
-    for _ in range(reps):
+    reps = 0
+    while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_seconds):
         oracle.verify_attention(w.q, w.kv_pool, w.kv_indices, w.prefix_lens, w.tree_mask, w.scale,
                                 heads=heads)
-    dt = (time.perf_counter() - t0) / reps
+        reps += 1
+    total = time.perf_counter() - t0
+    dt = total / reps
     scale_up = w.H / len(heads)
     what = "all heads" if len(heads) == w.H else f"heads {heads} of {w.H}, scaled by {scale_up:g}"
     return {
@@ -104,8 +115,8 @@ def cpu_baseline(w, heads, reps=1):
         "unit": "µs/call",
         "cores": blas_threads if blas_threads else len(os.sched_getaffinity(0)),
         "kind": "oracle",
-        "sample": f"oracle.verify_attention on the same workload ({what}), {reps} repetitions, "
-                  f"{dt:.2f} s each; host has {len(os.sched_getaffinity(0))} usable cores",
+        "sample": f"oracle.verify_attention on the same workload ({what}), {reps} calls in "
+                  f"{total:.1f} s; host has {len(os.sched_getaffinity(0))} usable cores",
     }
 
 
@@ -239,7 +250,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, heads=list(range(w.H)), reps=2)
+        result["cpu_baseline"] = cpu_baseline(w, heads=list(range(w.H)))
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -2,9 +2,11 @@
  * verify_attn.h -- C ABI of the MI355X (gfx950) MLA speculative-decoding
  * verify-attention library (libverify_attn.so).
  *
- * The operation (pages: "Building the paged sm120 verify kernel", section
- * "What This Build Achieves: The paged+bf16 Kernel"; "The Build That
- * Unlocked 3-6x Decode Speedup", section "The Context"):
+ * The operation (page "The Build That Bridged Design and Deployment:
+ * Compiling the Custom sm_120 Verify Kernel", section "What This Build
+ * Achieves: The paged+bf16 Kernel"; page "The Build That Unlocked 3-6x
+ * Decode Speedup", section "The Context: A Custom Kernel for an Unsupported
+ * Architecture"):
  *
  *   For every sequence b, query position i and head h, attend with the
  *   576-d query q[b][i][h] over the KV positions of sequence b. Position j
@@ -21,9 +23,12 @@
  *
  * The KV range of each sequence is split into chunks that run on separate
  * workgroups (flash-decode with online softmax over KV tiles); a second
- * kernel merges the chunk partials by log-sum-exp ("KV-split flash-decode",
- * NSPLIT: page "The Build That Unlocked ...", section "The Context"; page
- * "The Build Script Edit ...", section "Context").
+ * kernel merges the chunk partials by log-sum-exp (the KV split whose count
+ * the pages call NSPLIT: page "The Build That Unlocked 3-6x Decode Speedup", section "The
+ * Context: A Custom Kernel for an Unsupported Architecture"; page "The Build
+ * Script Edit: How a Single Line of Infrastructure Unlocked Custom CUDA
+ * Kernels on sm_120", section "Context: The Long Road to a Custom sm_120
+ * Kernel").
  *
  * Conventions for every entry point:
  *  - Device pointers are caller-owned device memory; the library allocates

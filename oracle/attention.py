@@ -4,9 +4,10 @@ TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, calls or links
 this module; only the test suite, the smoke check and the CPU-baseline leg of
 the benchmark use it. It shares no code with the GPU path.
 
-What is computed (pages: "Building the paged sm120 verify kernel", section
-"What This Build Achieves: The paged+bf16 Kernel"; "The Build That Unlocked
-3-6x Decode Speedup", section "The Context"):
+What is computed (page "The Build That Bridged Design and Deployment:
+Compiling the Custom sm_120 Verify Kernel", section "What This Build Achieves:
+The paged+bf16 Kernel"; page "The Build That Unlocked 3-6x Decode Speedup",
+section "The Context: A Custom Kernel for an Unsupported Architecture"):
 
 * KV rows are gathered through ``kv_indices`` with page_size 1: logical
   position j of sequence b is physical slot ``kv_indices[off_b + j]``.
@@ -28,10 +29,12 @@ the scale multiplies the fp64 dot product and is never folded into q.
 Besides the plain definition (``verify_attention``) this module carries two
 restatements of the pages' flash-decode method, used only to pin the oracle
 and to model the kernel's rounding: a KV split with a log-sum-exp merge
-(``split_merge_attention``; "KV-split flash-decode" / NSPLIT, page "The Build
-That Unlocked ...", section "The Context", and page "The Build Script Edit",
-section "Context") and online softmax over KV tiles
-(``online_softmax_attention``; same sections).
+(``split_merge_attention``; the flash-decode KV split with its NSPLIT
+parameter, page "The Build That Unlocked 3-6x Decode Speedup", section "The
+Context: A Custom Kernel for an Unsupported Architecture", and page "The Build
+Script Edit: How a Single Line of Infrastructure Unlocked Custom CUDA Kernels
+on sm_120", section "Context: The Long Road to a Custom sm_120 Kernel") and
+online softmax over KV tiles (``online_softmax_attention``; same sections).
 """
 
 from __future__ import annotations

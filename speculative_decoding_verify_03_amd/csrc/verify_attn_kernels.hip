@@ -1,8 +1,10 @@
 // HIP kernels for MLA speculative-decoding verify attention on gfx950 (MI355X).
 //
-// Method (pages: "The Build That Unlocked 3-6x Decode Speedup", section "The
-// Context"; "Building the paged sm120 verify kernel", section "What This Build
-// Achieves"): flash-decode. The KV positions of each sequence are cut into
+// Method (page "The Build That Unlocked 3-6x Decode Speedup", section "The
+// Context: A Custom Kernel for an Unsupported Architecture"; page "The Build
+// That Bridged Design and Deployment: Compiling the Custom sm_120 Verify
+// Kernel", section "What This Build Achieves: The paged+bf16 Kernel"):
+// flash-decode. The KV positions of each sequence are cut into
 // chunks; every (chunk, 128-row tile) pair is one workgroup that streams its
 // chunk through LDS in 32-key tiles with an online softmax, and a second
 // kernel merges the chunk partials by log-sum-exp.

@@ -1,8 +1,9 @@
 """Seeded input generators for MLA verify attention.
 
 The workload shapes follow the problem the pages describe (the paged bf16
-verify kernel of "Building the paged sm120 verify kernel", section "What This
-Build Achieves"): several requests per launch, each with its own prefix
+verify kernel of page "The Build That Bridged Design and Deployment: Compiling
+the Custom sm_120 Verify Kernel", section "What This Build Achieves: The
+paged+bf16 Kernel"): several requests per launch, each with its own prefix
 length, a page_size-1 KV pool addressed through ``kv_indices``, and a small
 q x q visibility matrix for the speculative tail. Latent width 576 with the
 first 512 dims as values, the 1/sqrt(192) scale, and the five concrete
