@@ -109,6 +109,15 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
 
+// The lane id, re-derived where it is used: as a volatile asm result it cannot
+// be hoisted out of a loop, so per-lane addresses built from it are
+// recomputed in place instead of occupying registers across the loop.
+__device__ __forceinline__ int fresh_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // bf16 x 4 (as raw bits, two per dword) -> fp16 x 4; exact for |v| in the
 // fp16 normal range.
 __device__ __forceinline__ void bf16x4_to_f16(u32x2 v, f16x8& dst, int base) {
@@ -206,12 +215,22 @@ constexpr int kLdsKSteps = kHalfKSteps - kRegKSteps;    // the rest are re-read 
 constexpr int kQParkBytes = kLdsKSteps * 64 * 16;       // per wave
 constexpr int kOffXchg = kRingS * kTileBytes;                      // 110592
 constexpr int kOffP = kOffXchg + kPairs * kXchgBytes;              // 126976
-constexpr int kOffAlpha = kOffP + kPairs * kPBytes;                // 135168
-constexpr int kOffFlag = kOffAlpha + kRowsPerWG * 4;               // 135680
-constexpr int kOffSlots = kOffFlag + 64;                           // 135744: slot-index ring
-constexpr int kSlotRing = 3;                                       // 256 bytes per tile
-constexpr int kOffQPark = kOffSlots + kSlotRing * 256;             // 136512
-constexpr int kSplitLds = kOffQPark + kSplitWaves * kQParkBytes;   // 152896
+constexpr int kOffAlpha = kOffP + 2 * kPairs * kPBytes;            // 143360: P, two tile parities
+constexpr int kOffFlag = kOffAlpha + 2 * kRowsPerWG * 4;           // 144384: rescale factors, two parities
+constexpr int kOffSlots = kOffFlag + 64;                           // 144448: slot-index ring
+constexpr int kSlotRing = 6;                                       // 256 bytes per tile
+constexpr int kSlotAhead = 5;                                      // slot copy distance, tiles
+constexpr int kPrefAhead = 4;                                      // L2 prefetch distance, tiles
+constexpr int kOffPref = kOffSlots + kSlotRing * 256;              // 145984: prefetch sink
+constexpr int kOffQPark = kOffPref + 256;                          // 146240
+constexpr int kSplitLds = kOffQPark + kSplitWaves * kQParkBytes;   // 162624
+static_assert(kSplitLds <= 160 * 1024, "split kernel LDS budget");
+static_assert(kSlotRing > kSlotAhead && kSlotAhead > kPrefAhead && kPrefAhead > 2, "slot ring distances");
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
 
 __global__ void __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 split_kernel(SplitArgs a) {
@@ -279,43 +298,51 @@ split_kernel(SplitArgs a) {
     }
   }
 
-  // Lane-constant LDS offsets.
+  // Lane-constant LDS offsets, recomputed where they are used (from
+  // fresh_lane(), so they do not occupy registers across the loop).
   // Score A operand: A-row n holds key swap_bits23(n), so that the score
   // accumulator element i of lane (n + 32h) is key 16*(i/8) + 8h + (i%8).
   // Its k-step ks of this wave reads chunk 2(18p + ks) + h; a_off[j] is the
   // address for ks = j, and ks = j + 4q adds q KiB.
-  const int arow_key = (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
-  int a_off[4];
+  auto score_offsets = [&](int (&a_off)[4]) {
+    const int fl = fresh_lane();
+    const int nn = fl & 31, hh = fl >> 5;
+    const int arow_key = (nn & ~12) | ((nn & 4) << 1) | ((nn & 8) >> 1);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) a_off[j] = tile_offset(2 * (kHalfKSteps * p + j) + h, arow_key);
+    for (int j = 0; j < 4; ++j) a_off[j] = tile_offset(2 * (kHalfKSteps * p + j) + hh, arow_key);
+  };
   // Value transpose reads: group g = lane/16, s = lane%16 supplies the address
   // of V[key 16t + 8h + 4hf + s/4][dv 32db + 16(g%2) + 4(s%4) .. +3] for this
   // wave's blocks db = 2w + d; key 16t adds 18 KiB (t is an immediate).
-  const int g = lane >> 4, s = lane & 15;
-  int tr_off[2][2];
+  auto value_offsets = [&](int (&tr_off)[2][2]) {
+    const int fl = fresh_lane();
+    const int g = fl >> 4, s = fl & 15, hh = fl >> 5;
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
+    for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-    for (int d = 0; d < 2; ++d)
-      tr_off[hf][d] = tile_offset(4 * (2 * wave + d) + 2 * (g & 1) + ((s & 3) >> 1), 8 * h + 4 * hf + (s >> 2)) +
-                      (s & 1) * 8;
+      for (int d = 0; d < 2; ++d)
+        tr_off[hf][d] = tile_offset(4 * (2 * wave + d) + 2 * (g & 1) + ((s & 3) >> 1), 8 * hh + 4 * hf + (s >> 2)) +
+                        (s & 1) * 8;
+  };
   LDS_AS char* xchg = lds + kOffXchg + pair * kXchgBytes + lane * 16;   // + k * 1024
   LDS_AS char* pbuf = lds + kOffP + lane * 16;                          // + rb * kPBytes + t * 1024
   LDS_AS char* abuf = lds + kOffAlpha;
   LDS_AS char* fbuf = lds + kOffFlag;
 
   // Gather bookkeeping (see gather_lane): even waves issue 5 loads per tile,
-  // odd waves 4; lane l always fetches key gl.key of a tile.
-  const GatherLane gl = gather_lane(wave, lane);
-  const int gkey = gl.key;
+  // odd waves 4; lane l always fetches the same key of a tile.
+  // (The per-lane gather fields are re-derived from fresh_lane() at each use,
+  // so they do not occupy registers across the loop.)
+  auto glane = [&]() { return gather_lane(wave, fresh_lane()); };
   // Slot indices travel through LDS like the latent rows: wave 0 copies the
-  // 32 kv_indices entries of tile v into ring entry v % 3 with one
-  // direct-to-LDS dword load (lanes 32-63 duplicate lanes 0-31), one tile
-  // before the gather that needs them, so the loop-top vmcnt wait covers them
-  // too. (A register load would make the compiler wait for it with a vmcnt
-  // that also drains the gathers issued after it.)
+  // 32 kv_indices entries of tile v into ring entry v % 6 with one
+  // direct-to-LDS dword load (lanes 32-63 duplicate lanes 0-31), three tiles
+  // before the gather that needs them and one before the L2 prefetch, so the
+  // loop-top vmcnt wait covers them too. (A register load would make the
+  // compiler wait for it with a vmcnt that also drains the gathers issued
+  // after it.)
   LDS_AS char* slot_ring = lds + kOffSlots;
-  auto tile_key_ok = [&](int v) -> bool { return kstart + (int64_t)v * kUnit + gkey < kend; };
+  auto tile_key_ok = [&](int v, int gkey) -> bool { return kstart + (int64_t)v * kUnit + gkey < kend; };
   auto load_slots_to_lds = [&](int v) {
     if (wave == 0) {
       int64_t gpos = sbase + kstart + (int64_t)v * kUnit + (lane & 31);
@@ -325,14 +352,35 @@ split_kernel(SplitArgs a) {
     }
   };
   auto read_slot = [&](int v) -> int32_t {
+    const int gkey = glane().key;
     const int32_t sl = *reinterpret_cast<LDS_AS const int32_t*>(slot_ring + (v % kSlotRing) * 256 + gkey * 4);
-    return tile_key_ok(v) ? sl : -1;
+    return tile_key_ok(v, gkey) ? sl : -1;
   };
   auto load_slot = [&](int v) -> int32_t {
-    const int64_t pos = kstart + (int64_t)v * kUnit + gkey;
+    const int64_t pos = kstart + (int64_t)v * kUnit + glane().key;
     return pos < kend ? a.kv_indices[sbase + pos] : -1;
   };
-  auto issue = [&](int32_t slot, LDS_AS char* tile) { issue_tile_gather(a.kv_pool, a.num_slots, slot, tile, gl); };
+  auto issue = [&](int32_t slot, LDS_AS char* tile) { issue_tile_gather(a.kv_pool, a.num_slots, slot, tile, glane()); };
+  // L2 prefetch, one direct-to-LDS dword load per odd-half wave and tile
+  // (into a sink that nothing reads): lane m = 64(w-4) + l touches line
+  // rt + row_tiles * m of tile v's 288 lines (9 per key), so the row tiles of
+  // a chunk, which run side by side on one XCD, bring each line into L2 once
+  // between them, ahead of the gathers. Always exactly one instruction (lanes
+  // without a line read the zero row), which keeps the loop-top vmcnt
+  // counts exact.
+  auto prefetch = [&](int v, bool live) {
+    const int fl = fresh_lane();
+    const int m = (wave - 4) * 64 + fl;
+    const int li = rt + a.row_tiles * m;
+    const int key = li / 9;
+    const int line = li - key * 9;
+    const char* ptr = reinterpret_cast<const char*>(g_zero_row);
+    if (live && li < 9 * kUnit && kstart + (int64_t)v * kUnit + key < kend) {
+      const int32_t sl = *reinterpret_cast<LDS_AS const int32_t*>(slot_ring + (v % kSlotRing) * 256 + key * 4);
+      if (sl >= 0 && sl < a.num_slots) ptr = a.kv_pool + (int64_t)sl * kRowBytes + line * 128;
+    }
+    __builtin_amdgcn_global_load_lds(ptr, lds + kOffPref, 4, 0, 0);
+  };
 
   // Online-softmax state of the pair's rows (log2 domain; kept by the even
   // half) and this wave's output accumulators O^T: [row block][value block].
@@ -344,165 +392,253 @@ split_kernel(SplitArgs a) {
 #pragma unroll
     for (int db = 0; db < kWaveDvBlocks; ++db) o[rb][db] = f32x16{};
 
-  // Prologue, in the same order as the loop body: [slots u+3][tile u+2].
-  {
-    const int32_t s0 = load_slot(0);
-    const int32_t s1 = load_slot(1);
-    issue(s0, lds);
-    load_slots_to_lds(2);
-    issue(s1, lds + kTileBytes);
-  }
-
-  for (int u = 0; u < nunits; ++u) {
-    // Since tile u went out, this wave issued the 5 or 4 loads of tile u+1
-    // (wave 0 also the slot copy of tile u+2, before them). Once no more than
-    // those gathers are outstanding, tile u and the slots of tile u+2 have
-    // landed (the compiler does not track direct-to-LDS loads, so this wait
-    // is explicit). The barrier is issued by hand so that it does
-    // not also drain the next tile's loads. It also
-    // guarantees that every wave is done with tile u-1 and with the P,
-    // rescale factors and flags of tile u-1.
-    if ((wave & 1) == 0) asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
-
-    LDS_AS char* tile = lds + (u % kRingS) * kTileBytes;
-    const int32_t slot_u2 = read_slot(u + 2);
-    load_slots_to_lds(u + 3);
-    issue(slot_u2, lds + ((u + 2) % kRingS) * kTileBytes);  // tile u-1's slot is free
-
-    // ---- partial scores S^T over this wave's 288 dims
-    f32x16 sa = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < kHalfKSteps; ++ks) {
-      const bf16x8 k0 = *reinterpret_cast<LDS_AS const bf16x8*>(tile + a_off[ks & 3] + (ks >> 2) * 1024);
-      const bf16x8 qv = ks < kRegKSteps
-                            ? qf[ks < kRegKSteps ? ks : 0]
-                            : *reinterpret_cast<LDS_AS const bf16x8*>(my_q + (ks - kRegKSteps) * 1024);
-      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qv, sa, 0, 0, 0);
-    }
-    if (p == 1) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        *reinterpret_cast<LDS_AS f32x4*>(xchg + k * 1024) =
-            f32x4{sa[4 * k], sa[4 * k + 1], sa[4 * k + 2], sa[4 * k + 3]};
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-
-    if (p == 0) {
-      // ---- full scores, mask, running max, lazy rescale, probabilities
-      float x[16];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const f32x4 d = *reinterpret_cast<LDS_AS const f32x4*>(xchg + k * 1024);
-        x[4 * k] = (sa[4 * k] + d[0]) * a.c_log2;
-        x[4 * k + 1] = (sa[4 * k + 1] + d[1]) * a.c_log2;
-        x[4 * k + 2] = (sa[4 * k + 2] + d[2]) * a.c_log2;
-        x[4 * k + 3] = (sa[4 * k + 3] + d[3]) * a.c_log2;
-      }
-      const int64_t ustart = kstart + (int64_t)u * kUnit;
-      if (ustart + kUnit > P || ustart + kUnit > kend) {
-        // Branch-free selects: a short-circuit form of this test was compiled
-        // into control flow that dropped the -inf store for hidden tail keys.
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int64_t pos = ustart + 16 * (i >> 3) + 8 * h + (i & 7);
-          const int64_t rel = pos - P;
-          const unsigned tail_bit = (unsigned)(tbits >> (unsigned)(rel & 63)) & 1u;
-          const unsigned vis = (unsigned)(pos < kend) & ((unsigned)(rel < 0) | tail_bit);
-          x[i] = vis ? x[i] : -INFINITY;
-        }
-      }
-      float mx = x[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const bool grow = mx > m_ref + kLazyRescale;  // false while the row has seen nothing
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.f;  // exp2(-inf) = 0
-      if (grow) m_ref = mx;
-      l_sum *= alpha;
-      const float mref_safe = m_ref == -INFINITY ? 0.f : m_ref;
-      f16x8 p0, p1;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float e0 = __builtin_amdgcn_exp2f(x[j] - mref_safe);
-        const float e1 = __builtin_amdgcn_exp2f(x[8 + j] - mref_safe);
-        l_sum += e0 + e1;
-        p0[j] = (_Float16)e0;
-        p1[j] = (_Float16)e1;
-      }
-      *reinterpret_cast<LDS_AS f16x8*>(pbuf + pair * kPBytes) = p0;
-      *reinterpret_cast<LDS_AS f16x8*>(pbuf + pair * kPBytes + 1024) = p1;
-      const int any_grow = __ballot(grow) != 0;  // wave-wide: taken before any lane is masked off
-      if (h == 0) *reinterpret_cast<LDS_AS float*>(abuf + (pair * 32 + n) * 4) = alpha;
-      if (lane == 0) *reinterpret_cast<LDS_AS int*>(fbuf + pair * 4) = any_grow;
-    }
-
-    // ---- this wave's value operands (independent of P): V^T for its two
-    // 32-dim blocks and both 16-key steps, transposed and converted to fp16
-    f16x8 va[kWaveDvBlocks][2];
-    {
-      // The eight transpose reads and their wait form one asm statement, so the
-      // outputs are complete when it ends. (As separate builtins the compiler
-      // fences each with vmcnt(0) against the direct-to-LDS loads in flight,
-      // which would drain the gather prefetch; split into an asm read plus a
-      // later wait, the compiler may copy a destination register before the
-      // data has arrived.)
-      u32x2 v[kWaveDvBlocks][2][2];   // [d][t][hf]
-      {
-        const unsigned a00 = (unsigned)(uintptr_t)(tile + tr_off[0][0]);
-        const unsigned a10 = (unsigned)(uintptr_t)(tile + tr_off[1][0]);
-        const unsigned a01 = (unsigned)(uintptr_t)(tile + tr_off[0][1]);
-        const unsigned a11 = (unsigned)(uintptr_t)(tile + tr_off[1][1]);
-        asm volatile(
-            "ds_read_b64_tr_b16 %0, %8\n\t"
-            "ds_read_b64_tr_b16 %1, %9\n\t"
-            "ds_read_b64_tr_b16 %2, %8 offset:18432\n\t"
-            "ds_read_b64_tr_b16 %3, %9 offset:18432\n\t"
-            "ds_read_b64_tr_b16 %4, %10\n\t"
-            "ds_read_b64_tr_b16 %5, %11\n\t"
-            "ds_read_b64_tr_b16 %6, %10 offset:18432\n\t"
-            "ds_read_b64_tr_b16 %7, %11 offset:18432\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(v[0][0][0]), "=&v"(v[0][0][1]), "=&v"(v[0][1][0]), "=&v"(v[0][1][1]),
-              "=&v"(v[1][0][0]), "=&v"(v[1][0][1]), "=&v"(v[1][1][0]), "=&v"(v[1][1][1])
-            : "v"(a00), "v"(a10), "v"(a01), "v"(a11)
-            : "memory");
-      }
-      // all LDS stores of this iteration (P/alpha/flag of the even half) are
-      // complete before the barrier
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-#pragma unroll
-      for (int db = 0; db < kWaveDvBlocks; ++db)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          bf16x4_to_f16(v[db][t][0], va[db][t], 0);
-          bf16x4_to_f16(v[db][t][1], va[db][t], 4);
-        }
-    }
-
-    // ---- rescale O for row blocks whose running max grew (rare)
-    const i32x4 flags = *reinterpret_cast<LDS_AS const i32x4*>(fbuf);
+  // P, rescale factors and rescale flags are double-buffered by tile parity:
+  // the odd half applies tile u-1 while the even half publishes tile u.
+  auto pbuf_of = [&](int v) { return pbuf + (v & 1) * (kPairs * kPBytes); };
+  auto abuf_of = [&](int v) { return abuf + (v & 1) * (kRowsPerWG * 4); };
+  auto fbuf_of = [&](int v) { return fbuf + (v & 1) * 16; };
+  // O^T *= alpha(v) for row blocks whose running max grew in tile v (rare).
+  auto rescale = [&](int v) {
+    const i32x4 flags = *reinterpret_cast<LDS_AS const i32x4*>(fbuf_of(v));
     if (flags[0] | flags[1] | flags[2] | flags[3]) {
 #pragma unroll
       for (int rb = 0; rb < kRowBlocks; ++rb) {
-        const float al = *reinterpret_cast<LDS_AS const float*>(abuf + (rb * 32 + n) * 4);
+        const float al = *reinterpret_cast<LDS_AS const float*>(abuf_of(v) + (rb * 32 + n) * 4);
 #pragma unroll
         for (int db = 0; db < kWaveDvBlocks; ++db) o[rb][db] *= al;
       }
     }
-
-    // ---- O^T += V^T P^T for this wave's 64 dims and all 128 rows
+  };
+  // O^T += V(v)^T P(v)^T for this wave's 64 dims and all 128 rows.
+  auto apply_values = [&](int v, const f16x8 (&va)[kWaveDvBlocks][2]) {
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb) {
-      const f16x8 pb0 = *reinterpret_cast<LDS_AS const f16x8*>(pbuf + rb * kPBytes);
-      const f16x8 pb1 = *reinterpret_cast<LDS_AS const f16x8*>(pbuf + rb * kPBytes + 1024);
+      const f16x8 pb0 = *reinterpret_cast<LDS_AS const f16x8*>(pbuf_of(v) + rb * kPBytes);
+      const f16x8 pb1 = *reinterpret_cast<LDS_AS const f16x8*>(pbuf_of(v) + rb * kPBytes + 1024);
+      // key step outer, so consecutive MFMAs are independent
 #pragma unroll
-      for (int db = 0; db < kWaveDvBlocks; ++db) {
+      for (int db = 0; db < kWaveDvBlocks; ++db)
         o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[db][0], pb0, o[rb][db], 0, 0, 0);
+#pragma unroll
+      for (int db = 0; db < kWaveDvBlocks; ++db)
         o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[db][1], pb1, o[rb][db], 0, 0, 0);
+    }
+  };
+
+  // One half's pipeline (PP = p). The even half computes its share of the
+  // scores of tile u, runs the softmax, and applies tile u after the second
+  // barrier. The odd half computes its share of the scores, then applies
+  // tile u-1 while the even half runs the softmax of tile u (keeping the
+  // matrix cores busy), and reads the values of tile u for the next
+  // iteration. Both copies execute the same barriers.
+  auto run = [&](auto pc) {
+    constexpr int PP = decltype(pc)::value;
+
+    // Prologue, in the same order as the loop body: [slots][tile u+2][prefetch]
+    // (the prologue's two prefetches touch nothing; they keep the counts).
+    {
+      const int32_t s0 = load_slot(0);
+      const int32_t s1 = load_slot(1);
+      issue(s0, lds);
+      for (int v = 2; v < kSlotAhead; ++v) load_slots_to_lds(v);
+      if constexpr (PP == 1) prefetch(0, false);
+      issue(s1, lds + kTileBytes);
+      if constexpr (PP == 1) prefetch(0, false);
+    }
+
+    f16x8 vheld[kWaveDvBlocks][2];   // odd half: values of the previous tile
+#pragma unroll
+    for (int db = 0; db < kWaveDvBlocks; ++db) vheld[db][0] = vheld[db][1] = f16x8{};
+
+    for (int u = 0; u < nunits; ++u) {
+      // Since tile u went out, this wave issued the 5 or 4 loads of tile u+1
+      // (wave 0 also the slot copy of tile u+4, before them; the odd half
+      // also one prefetch after each of the last two gathers). Once no more
+      // than those are outstanding, tile u and the slots of tile u+4 have
+      // landed (the compiler does not track direct-to-LDS loads, so this wait
+      // is explicit). The barrier is issued by hand so that it does not also
+      // drain the next tile's loads. It also guarantees that every wave is
+      // done with tile u-1 (the odd half holds its values in registers).
+      if constexpr (PP == 0) {
+        if ((wave & 1) == 0) asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+      } else {
+        if ((wave & 1) == 0) asm volatile("s_waitcnt vmcnt(7)\n\ts_barrier" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
+      }
+
+      LDS_AS char* tile = lds + (u % kRingS) * kTileBytes;
+      const int32_t slot_u2 = read_slot(u + 2);
+      load_slots_to_lds(u + kSlotAhead);
+      issue(slot_u2, lds + ((u + 2) % kRingS) * kTileBytes);  // tile u-1's slot is free
+
+      // ---- partial scores S^T over this wave's 288 dims. The K operands (and
+      // parked queries) are read kDepth k-steps ahead of their MFMA; the
+      // scheduling barriers keep the compiler from sinking each read next to
+      // its use, which would expose one LDS round trip per MFMA.
+      f32x16 sa = f32x16{};
+      {
+        int a_off[4];
+        score_offsets(a_off);
+        constexpr int kDepth = 3;    // K reads in flight
+        constexpr int kQDepth = 2;   // parked-query reads in flight
+        auto kload = [&](int ks) {
+          return *reinterpret_cast<LDS_AS const bf16x8*>(tile + a_off[ks & 3] + (ks >> 2) * 1024);
+        };
+        auto qpark = [&](int ks) {
+          return *reinterpret_cast<LDS_AS const bf16x8*>(my_q + (ks - kRegKSteps) * 1024);
+        };
+        bf16x8 kb[kDepth], qb[kQDepth];
+#pragma unroll
+        for (int i = 0; i < kDepth; ++i) kb[i] = kload(i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < kHalfKSteps; ++ks) {
+          const bf16x8 kc = kb[ks % kDepth];
+          const bf16x8 qc = ks < kRegKSteps ? qf[ks < kRegKSteps ? ks : 0] : qb[ks % kQDepth];
+          if (ks + kDepth < kHalfKSteps) kb[ks % kDepth] = kload(ks + kDepth);
+          if (ks + kQDepth >= kRegKSteps && ks + kQDepth < kHalfKSteps) qb[ks % kQDepth] = qpark(ks + kQDepth);
+          sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qc, sa, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if constexpr (PP == 1) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          *reinterpret_cast<LDS_AS f32x4*>(xchg + k * 1024) =
+              f32x4{sa[4 * k], sa[4 * k + 1], sa[4 * k + 2], sa[4 * k + 3]};
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+      if constexpr (PP == 1) {
+        // ---- while the even half runs the softmax: prefetch, then apply the
+        // previous tile
+        prefetch(u + kPrefAhead, true);
+        if (u > 0) {
+          rescale(u - 1);
+          apply_values(u - 1, vheld);
+        }
+      } else {
+        // ---- full scores, mask, running max, lazy rescale, probabilities
+        float x[16];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const f32x4 d = *reinterpret_cast<LDS_AS const f32x4*>(xchg + k * 1024);
+          x[4 * k] = (sa[4 * k] + d[0]) * a.c_log2;
+          x[4 * k + 1] = (sa[4 * k + 1] + d[1]) * a.c_log2;
+          x[4 * k + 2] = (sa[4 * k + 2] + d[2]) * a.c_log2;
+          x[4 * k + 3] = (sa[4 * k + 3] + d[3]) * a.c_log2;
+        }
+        const int64_t ustart = kstart + (int64_t)u * kUnit;
+        if (ustart + kUnit > P || ustart + kUnit > kend) {
+          // Positions relative to the tile start fit in 32 bits (a chunk is
+          // at most 2^31 keys). Branch-free selects: a short-circuit form of
+          // this test was compiled into control flow that dropped the -inf
+          // store for hidden tail keys.
+          const int rel0 = (int)(ustart - P);
+          const int end0 = (int)(kend - ustart);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kk = 16 * (i >> 3) + 8 * h + (i & 7);
+            const int rel = rel0 + kk;
+            const unsigned tail_bit = (unsigned)(tbits >> (unsigned)(rel & 63)) & 1u;
+            const unsigned vis = (unsigned)(kk < end0) & ((unsigned)(rel < 0) | tail_bit);
+            x[i] = vis ? x[i] : -INFINITY;
+          }
+        }
+        float mx = x[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+        mx = fmaxf(mx, swap_halves(mx));
+        const bool grow = mx > m_ref + kLazyRescale;  // false while the row has seen nothing
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.f;  // exp2(-inf) = 0
+        if (grow) m_ref = mx;
+        l_sum *= alpha;
+        const float mref_safe = m_ref == -INFINITY ? 0.f : m_ref;
+        f16x8 p0, p1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float e0 = __builtin_amdgcn_exp2f(x[j] - mref_safe);
+          const float e1 = __builtin_amdgcn_exp2f(x[8 + j] - mref_safe);
+          l_sum += e0 + e1;
+          p0[j] = (_Float16)e0;
+          p1[j] = (_Float16)e1;
+        }
+        *reinterpret_cast<LDS_AS f16x8*>(pbuf_of(u) + pair * kPBytes) = p0;
+        *reinterpret_cast<LDS_AS f16x8*>(pbuf_of(u) + pair * kPBytes + 1024) = p1;
+        const int any_grow = __ballot(grow) != 0;  // wave-wide: taken before any lane is masked off
+        if (h == 0) *reinterpret_cast<LDS_AS float*>(abuf_of(u) + (pair * 32 + n) * 4) = alpha;
+        if (lane == 0) *reinterpret_cast<LDS_AS int*>(fbuf_of(u) + pair * 4) = any_grow;
+      }
+
+      // ---- this wave's value operands of tile u: V^T for its two 32-dim
+      // blocks and both 16-key steps, transposed and converted to fp16
+      f16x8 va[kWaveDvBlocks][2];
+      {
+        // The eight transpose reads and their wait form one asm statement, so
+        // the outputs are complete when it ends. (As separate builtins the
+        // compiler fences each with vmcnt(0) against the direct-to-LDS loads
+        // in flight, which would drain the gather prefetch; split into an asm
+        // read plus a later wait, the compiler may copy a destination register
+        // before the data has arrived.) The leading s_nop keeps the new
+        // register writes clear of operand reads of MFMAs still in flight.
+        u32x2 v[kWaveDvBlocks][2][2];   // [d][t][hf]
+        {
+          int tr_off[2][2];
+          value_offsets(tr_off);
+          const unsigned a00 = (unsigned)(uintptr_t)(tile + tr_off[0][0]);
+          const unsigned a10 = (unsigned)(uintptr_t)(tile + tr_off[1][0]);
+          const unsigned a01 = (unsigned)(uintptr_t)(tile + tr_off[0][1]);
+          const unsigned a11 = (unsigned)(uintptr_t)(tile + tr_off[1][1]);
+          asm volatile(
+              "s_nop 7\n\t"
+              "ds_read_b64_tr_b16 %0, %8\n\t"
+              "ds_read_b64_tr_b16 %1, %9\n\t"
+              "ds_read_b64_tr_b16 %2, %8 offset:18432\n\t"
+              "ds_read_b64_tr_b16 %3, %9 offset:18432\n\t"
+              "ds_read_b64_tr_b16 %4, %10\n\t"
+              "ds_read_b64_tr_b16 %5, %11\n\t"
+              "ds_read_b64_tr_b16 %6, %10 offset:18432\n\t"
+              "ds_read_b64_tr_b16 %7, %11 offset:18432\n\t"
+              "s_waitcnt lgkmcnt(0)"
+              : "=&v"(v[0][0][0]), "=&v"(v[0][0][1]), "=&v"(v[0][1][0]), "=&v"(v[0][1][1]),
+                "=&v"(v[1][0][0]), "=&v"(v[1][0][1]), "=&v"(v[1][1][0]), "=&v"(v[1][1][1])
+              : "v"(a00), "v"(a10), "v"(a01), "v"(a11)
+              : "memory");
+        }
+        // all LDS stores of this iteration (P/alpha/flag of the even half)
+        // are complete before the barrier
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int db = 0; db < kWaveDvBlocks; ++db)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            bf16x4_to_f16(v[db][t][0], va[db][t], 0);
+            bf16x4_to_f16(v[db][t][1], va[db][t], 4);
+          }
+      }
+
+      if constexpr (PP == 0) {
+        rescale(u);
+        apply_values(u, va);
+      } else {
+#pragma unroll
+        for (int db = 0; db < kWaveDvBlocks; ++db) {
+          vheld[db][0] = va[db][0];
+          vheld[db][1] = va[db][1];
+        }
       }
     }
-  }
+    // the odd half's value update of the last tile
+    if constexpr (PP == 1) {
+      if (nunits > 0) {
+        rescale(nunits - 1);
+        apply_values(nunits - 1, vheld);
+      }
+    }
+  };
+  if (p == 0) run(IntC<0>{});
+  else run(IntC<1>{});
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain prefetches before exit
 
   // ---- epilogue: the even halves publish 1/l per row (reusing the alpha
