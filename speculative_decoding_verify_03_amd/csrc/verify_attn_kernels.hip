@@ -675,36 +675,88 @@ split_kernel(SplitArgs a) {
 
 // ---------------------------------------------------------------------------
 // Merge: lse = ln sum_s exp(lse_s); out = sum_s exp(lse_s - lse) O_s.
-// Two rows per 256-thread workgroup, 4 value dims per thread.
+// One 256-thread workgroup per (row, quarter of the 512 value dims): thread
+// t handles 4 dims (t % 32) of the quarter for chunks c0 + (t / 32) + 8k, so
+// each wave reads two whole 512-byte row segments per step and the chunks
+// of a row are spread over 8 lanes; an LDS reduction combines them.
 // ---------------------------------------------------------------------------
+constexpr int kMergeLanes = 8;   // chunk lanes per workgroup
+
 __global__ void __launch_bounds__(256) merge_kernel(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_lse,
                                                     const int32_t* __restrict__ chunk_off,
                                                     float* __restrict__ out, float* __restrict__ lse,
                                                     int B, int R) {
-  const int64_t grow = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
+  __shared__ float s_max[256];
+  __shared__ f32x4 s_acc[kMergeLanes][32];
+  __shared__ float s_w[kMergeLanes];
+  const int64_t grow = (int64_t)(blockIdx.x >> 2);
+  const int qd = blockIdx.x & 3;
   if (grow >= (int64_t)B * R) return;
   const int b = (int)(grow / R);
   const int r = (int)(grow - (int64_t)b * R);
-  const int t = threadIdx.x & 127;
+  const int t = threadIdx.x;
+  const int dl = t & 31, cl = t >> 5;
   const int c0 = chunk_off[b], c1 = chunk_off[b + 1];
+
+  // max of the partial lse over the row's chunks
   float mx = -INFINITY;
-  for (int c = c0; c < c1; ++c) mx = fmaxf(mx, part_lse[(int64_t)c * R + r]);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float lse_v = -INFINITY;
-  if (mx > -INFINITY) {
-    float wsum = 0.f;
-    for (int c = c0; c < c1; ++c) {
-      const float w = __builtin_amdgcn_exp2f((part_lse[(int64_t)c * R + r] - mx) * kLog2e);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(part_o + ((int64_t)c * R + r) * kValue + 4 * t);
-      acc += w * v;
-      wsum += w;
-    }
-    acc *= 1.f / wsum;
-    lse_v = mx + __builtin_amdgcn_logf(wsum) * kLn2;
+  for (int c = c0 + t; c < c1; c += 256) mx = fmaxf(mx, part_lse[(int64_t)c * R + r]);
+  s_max[t] = mx;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (t < off) s_max[t] = fmaxf(s_max[t], s_max[t + off]);
+    __syncthreads();
   }
-  *reinterpret_cast<f32x4*>(out + grow * kValue + 4 * t) = acc;
-  if (t == 0) lse[grow] = lse_v;
+  mx = s_max[0];
+
+  float* orow = out + grow * kValue + qd * 128 + 4 * dl;
+  if (!(mx > -INFINITY)) {   // nothing visible in any chunk
+    if (cl == 0) *reinterpret_cast<f32x4*>(orow) = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (t == 0 && qd == 0) lse[grow] = -INFINITY;
+    return;
+  }
+  // weighted sums over this lane's chunks (weights exp(lse_s - max); empty
+  // chunks have lse_s = -inf and weight 0)
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  const float* obase = part_o + (int64_t)r * kValue + qd * 128 + 4 * dl;
+  int c = c0 + cl;
+  for (; c + 3 * kMergeLanes < c1; c += 4 * kMergeLanes) {
+    float w[4];
+    f32x4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t ck = c + k * kMergeLanes;
+      w[k] = part_lse[ck * R + r];
+      v[k] = *reinterpret_cast<const f32x4*>(obase + ck * R * kValue);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float wk = __builtin_amdgcn_exp2f((w[k] - mx) * kLog2e);
+      acc += wk * v[k];
+      wsum += wk;
+    }
+  }
+  for (; c < c1; c += kMergeLanes) {
+    const float wk = __builtin_amdgcn_exp2f((part_lse[(int64_t)c * R + r] - mx) * kLog2e);
+    acc += wk * *reinterpret_cast<const f32x4*>(obase + (int64_t)c * R * kValue);
+    wsum += wk;
+  }
+  s_acc[cl][dl] = acc;
+  if (dl == 0) s_w[cl] = wsum;
+  __syncthreads();
+  if (cl == 0) {
+    f32x4 tot = s_acc[0][dl];
+    float wt = s_w[0];
+#pragma unroll
+    for (int k = 1; k < kMergeLanes; ++k) {
+      tot += s_acc[k][dl];
+      wt += s_w[k];
+    }
+    *reinterpret_cast<f32x4*>(orow) = tot * (1.f / wt);
+    if (dl == 0 && qd == 0) lse[grow] = mx + __builtin_amdgcn_logf(wt) * kLn2;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -752,7 +804,7 @@ hipError_t launch_split(const SplitArgs& a, int grid, hipStream_t stream) {
 hipError_t launch_merge(const float* part_o, const float* part_lse, const int32_t* chunk_off,
                         float* out, float* lse, int B, int R, hipStream_t stream) {
   const int64_t rows = (int64_t)B * R;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((rows + 1) / 2)), dim3(256), 0, stream, part_o,
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(rows * 4)), dim3(256), 0, stream, part_o,
                      part_lse, chunk_off, out, lse, B, R);
   return hipGetLastError();
 }
