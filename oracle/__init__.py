@@ -1,4 +1,5 @@
-"""CPU oracle for MLA speculative-decoding verify attention (test infrastructure).
+"""CPU oracle for MLA speculative-decoding verify attention and the steps next to
+it, KV defragmentation and draft-tree acceptance (test infrastructure).
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg may use
 this package; the product path never imports it. Every function is plain
@@ -25,3 +26,5 @@ from .attention import (  # noqa: F401
     online_softmax_attention,
     brute_force,
 )
+from .kvcache import defrag  # noqa: F401
+from .tree import tree_accept, tree_accept_batch  # noqa: F401

@@ -1,7 +1,7 @@
 """Seeded synthetic inputs for MLA speculative-decoding verify attention.
 
 This package only *generates* inputs (random numbers, permutations, draft
-trees, bf16 encoding of the generated floats). It holds none of the attention
+trees, draft and target tokens, bf16 encoding of the generated floats). It holds none of the attention
 arithmetic: both the CPU oracle and the GPU path consume what it produces, and
 neither shares any other code with the other.
 """
@@ -19,4 +19,5 @@ from .gen import (  # noqa: F401
     random_parents,
     make_config,
     make_workload,
+    make_tree_accept_case,
 )

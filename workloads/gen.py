@@ -211,3 +211,32 @@ def make_config(name: str) -> Workload:
     kw = dict(CONFIGS[name])
     seed = kw.pop("seed")
     return make_workload(name, seed, **kw)
+
+
+def make_tree_accept_case(seed: int, B: int, Q: int, vocab: int = 32000, p_follow: float = 0.7,
+                          max_depth: int = 8, chain: bool = False):
+    """Seeded inputs for draft-tree acceptance: parents int32 [B, Q] (parents[b, 0] = -1,
+    parents[b, i] < i), draft tokens and target tokens int32 [B, Q].
+
+    Draft tokens are uniform over the vocabulary. The target token at node i
+    copies the draft token of one of i's children (chosen uniformly) with
+    probability p_follow, so that paths of several tokens occur; otherwise it
+    is uniform too. Streams: 0 = tree shape, 1 = draft tokens, 2 = target tokens.
+    """
+    g_tree = np.random.default_rng([seed, 0])
+    g_draft = np.random.default_rng([seed, 1])
+    g_tgt = np.random.default_rng([seed, 2])
+    parents = np.empty((B, Q), np.int32)
+    draft = g_draft.integers(0, vocab, size=(B, Q), dtype=np.int64).astype(np.int32)
+    target = np.empty((B, Q), np.int32)
+    for b in range(B):
+        par = np.arange(-1, Q - 1, dtype=np.int32) if chain else random_parents(Q, g_tree, max_depth)
+        parents[b] = par
+        for i in range(Q):
+            kids = np.nonzero(par == i)[0]
+            kids = kids[kids != 0]
+            if kids.size and g_tgt.random() < p_follow:
+                target[b, i] = draft[b, kids[g_tgt.integers(0, kids.size)]]
+            else:
+                target[b, i] = g_tgt.integers(0, vocab)
+    return parents, draft, target
