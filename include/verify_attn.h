@@ -141,6 +141,62 @@ void verify_attn_set_split_events(void* start_event, void* stop_event);
  */
 void verify_attn_set_chunk_override(int32_t chunk_keys);
 
+/*
+ * KV-cache defragmentation (page "The Build That Unlocked 3-6x Decode
+ * Speedup", sections "The Context: A Custom Kernel for an Unsupported
+ * Architecture" and "The Broader Significance", where it is named as the step
+ * after the verify kernel; the pages give no more, and this is the plainest
+ * reading). For j = 0 .. n-1:
+ *     dst_pool[dst_base + j] = src_pool[kv_indices[j]]   (an all-zero row if
+ *                                                          the slot is outside
+ *                                                          [0, num_slots))
+ *     new_indices[j]         = dst_base + j
+ * Other destination rows are not touched. verify_attn() over (dst_pool,
+ * new_indices) then equals verify_attn() over (src_pool, kv_indices) bit for
+ * bit, and its gather reads consecutive rows.
+ *
+ *  src_pool    bf16 [num_slots][576], 16-byte aligned (read).
+ *  kv_indices  int32 [n] (read).
+ *  dst_pool    bf16 [dst_slots][576], 16-byte aligned (rows dst_base ..
+ *              dst_base + n - 1 written).
+ *  new_indices int32 [n] (written); may not alias kv_indices.
+ *  0 <= n <= 2^31 - 1; 0 <= dst_base <= dst_slots - n; dst_base + n - 1 must
+ *  fit in int32.
+ * The destination run must not overlap any row the source indices name (the
+ * host cannot check this; dst_pool may be src_pool when the run lies in free
+ * slots). Returns VA_OK, VA_EINVAL (nothing enqueued) or VA_EHIP.
+ */
+int verify_attn_kv_defrag(const void* src_pool, const int32_t* kv_indices, int64_t n, int64_t num_slots,
+                          void* dst_pool, int64_t dst_base, int64_t dst_slots, int32_t* new_indices,
+                          void* stream);
+
+/*
+ * Draft-tree acceptance (the tree_accept kernel source listed next to the
+ * verify kernels, page "The Build That Unlocked 3-6x Decode Speedup", section
+ * "Why This Build Was Different"; page "The Build Script Edit: How a Single
+ * Line of Infrastructure Unlocked Custom CUDA Kernels on sm_120", section
+ * "Input Knowledge Required"; the pages give only the name, and this is the
+ * plainest reading of greedy tree speculative decoding). For every sequence
+ * b, node 0 is the root (the last accepted token) and node i >= 1 has parent
+ * parents[b][i] < i and draft token draft_tokens[b][i]; target_tokens[b][i]
+ * is the target model's choice after the path root -> i. Starting at the
+ * root, the walk steps to the smallest-index child c of the current node
+ * with draft_tokens[b][c] == target_tokens[b][current] until no child
+ * matches.
+ *
+ *  parents, draft_tokens, target_tokens  int32 [B][Q] (read).
+ *  accept_len   int32 [B] (written): accepted draft tokens (path length - 1).
+ *  accepted     int32 [B][Q] (written): the path's node indices, root first,
+ *               then -1.
+ *  bonus_token  int32 [B] (written): target_tokens at the last accepted node.
+ *  B >= 1, 1 <= Q <= 64. A malformed tree (parents[i] >= i) cannot hang the
+ *  walk: only children with a larger index than the current node count.
+ * Returns VA_OK, VA_EINVAL (nothing enqueued) or VA_EHIP.
+ */
+int verify_attn_tree_accept(const int32_t* parents, const int32_t* draft_tokens, const int32_t* target_tokens,
+                            int B, int Q, int32_t* accept_len, int32_t* accepted, int32_t* bonus_token,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

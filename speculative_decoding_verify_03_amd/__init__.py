@@ -29,6 +29,8 @@ EXPORTED = (
     "verify_attn_query_plan",
     "verify_attn_set_chunk_override",
     "verify_attn_set_split_events",
+    "verify_attn_kv_defrag",
+    "verify_attn_tree_accept",
 )
 
 _lib = None
@@ -69,6 +71,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.verify_attn_set_chunk_override.restype = None
     lib.verify_attn_set_split_events.argtypes = [vp, vp]
     lib.verify_attn_set_split_events.restype = None
+    lib.verify_attn_kv_defrag.argtypes = [vp, vp, i64, i64, vp, i64, i64, vp, vp]
+    lib.verify_attn_kv_defrag.restype = i32
+    lib.verify_attn_tree_accept.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp]
+    lib.verify_attn_tree_accept.restype = i32
     _lib = lib
     return lib
 
@@ -169,3 +175,40 @@ def debug_gather(kv_pool, kv_indices, stream=None):
                                                    int(kv_pool.shape[0]), _ptr(rows),
                                                    _stream_handle(stream)))
     return rows
+
+
+def kv_defrag(src_pool, kv_indices, dst_pool, dst_base: int, new_indices=None, stream=None):
+    """Copy the rows kv_indices names into dst_pool[dst_base:dst_base+n] in position
+    order and return the rewritten index table (see include/verify_attn.h)."""
+    import torch
+    for name, t in (("src_pool", src_pool), ("kv_indices", kv_indices), ("dst_pool", dst_pool)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous CUDA tensor")
+    if kv_indices.dtype != torch.int32:
+        raise ValueError("kv_indices must be int32")
+    n = int(kv_indices.numel())
+    if new_indices is None:
+        new_indices = torch.empty(n, dtype=torch.int32, device=kv_indices.device)
+    _check(load_library().verify_attn_kv_defrag(_ptr(src_pool), _ptr(kv_indices), n, int(src_pool.shape[0]),
+                                                _ptr(dst_pool), int(dst_base), int(dst_pool.shape[0]),
+                                                _ptr(new_indices), _stream_handle(stream)))
+    return new_indices
+
+
+def tree_accept(parents, draft_tokens, target_tokens, out=None, stream=None):
+    """Greedy acceptance over draft trees, int32 [B, Q] inputs; returns
+    (accept_len [B], accepted [B, Q], bonus_token [B]) (see include/verify_attn.h)."""
+    import torch
+    B, Q = parents.shape
+    for name, t in (("parents", parents), ("draft_tokens", draft_tokens), ("target_tokens", target_tokens)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.int32 or tuple(t.shape) != (B, Q):
+            raise ValueError(f"{name} must be a contiguous int32 CUDA tensor [B, Q]")
+    if out is None:
+        dev = parents.device
+        out = (torch.empty(B, dtype=torch.int32, device=dev), torch.empty((B, Q), dtype=torch.int32, device=dev),
+               torch.empty(B, dtype=torch.int32, device=dev))
+    accept_len, accepted, bonus = out
+    _check(load_library().verify_attn_tree_accept(_ptr(parents), _ptr(draft_tokens), _ptr(target_tokens), B, Q,
+                                                  _ptr(accept_len), _ptr(accepted), _ptr(bonus),
+                                                  _stream_handle(stream)))
+    return accept_len, accepted, bonus

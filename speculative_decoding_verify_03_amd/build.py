@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libverify_attn.so")
-SOURCES = ["verify_attn_kernels.hip", "capi.cpp"]
+SOURCES = ["verify_attn_kernels.hip", "cache_kernels.hip", "capi.cpp"]
 ARCH = "gfx950"
 
 

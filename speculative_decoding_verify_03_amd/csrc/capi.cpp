@@ -226,4 +226,48 @@ int verify_attn_debug_gather(const void* kv_pool, const int32_t* kv_indices, int
   }
 }
 
+int verify_attn_kv_defrag(const void* src_pool, const int32_t* kv_indices, int64_t n, int64_t num_slots,
+                          void* dst_pool, int64_t dst_base, int64_t dst_slots, int32_t* new_indices,
+                          void* stream) {
+  try {
+    if (n < 0 || n > (int64_t)INT32_MAX) return fail(VA_EINVAL, "bad n %lld", (long long)n);
+    if (n == 0) return ok();
+    if (!src_pool || !kv_indices || !dst_pool || !new_indices) return fail(VA_EINVAL, "null pointer argument");
+    if (!aligned(src_pool, 16) || !aligned(dst_pool, 16) || !aligned(kv_indices, 4) || !aligned(new_indices, 4))
+      return fail(VA_EINVAL, "pools must be 16-byte and index arrays 4-byte aligned");
+    if (num_slots < 1 || num_slots > INT64_MAX / va::kRowBytes)
+      return fail(VA_EINVAL, "bad num_slots %lld", (long long)num_slots);
+    if (dst_slots < 1 || dst_slots > INT64_MAX / va::kRowBytes)
+      return fail(VA_EINVAL, "bad dst_slots %lld", (long long)dst_slots);
+    if (dst_base < 0 || dst_base > dst_slots - n || dst_base + n - 1 > (int64_t)INT32_MAX)
+      return fail(VA_EINVAL, "destination run [%lld, %lld) outside [0, %lld) or past int32 slots",
+                  (long long)dst_base, (long long)(dst_base + n), (long long)dst_slots);
+    hipError_t e = va::launch_defrag(src_pool, kv_indices, n, num_slots, dst_pool, dst_base, new_indices,
+                                     static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(VA_EHIP, "defrag launch: %s", hipGetErrorString(e));
+    return ok();
+  } catch (...) {
+    return fail(VA_EHIP, "unexpected C++ exception");
+  }
+}
+
+int verify_attn_tree_accept(const int32_t* parents, const int32_t* draft_tokens, const int32_t* target_tokens,
+                            int B, int Q, int32_t* accept_len, int32_t* accepted, int32_t* bonus_token,
+                            void* stream) {
+  try {
+    if (B < 1 || Q < 1 || Q > VA_MAX_Q) return fail(VA_EINVAL, "bad B=%d or Q=%d", B, Q);
+    if (!parents || !draft_tokens || !target_tokens || !accept_len || !accepted || !bonus_token)
+      return fail(VA_EINVAL, "null pointer argument");
+    if (!aligned(parents, 4) || !aligned(draft_tokens, 4) || !aligned(target_tokens, 4) ||
+        !aligned(accept_len, 4) || !aligned(accepted, 4) || !aligned(bonus_token, 4))
+      return fail(VA_EINVAL, "arrays must be 4-byte aligned");
+    hipError_t e = va::launch_tree_accept(parents, draft_tokens, target_tokens, B, Q, accept_len, accepted,
+                                          bonus_token, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(VA_EHIP, "tree accept launch: %s", hipGetErrorString(e));
+    return ok();
+  } catch (...) {
+    return fail(VA_EHIP, "unexpected C++ exception");
+  }
+}
+
 }  // extern "C"

@@ -56,5 +56,10 @@ hipError_t launch_merge(const float* part_o, const float* part_lse, const int32_
                         float* out, float* lse, int B, int R, hipStream_t stream);
 hipError_t launch_debug_gather(const void* kv_pool, const int32_t* kv_indices, int64_t n,
                                int64_t num_slots, void* rows_out, hipStream_t stream);
+hipError_t launch_defrag(const void* src_pool, const int32_t* kv_indices, int64_t n, int64_t num_slots,
+                         void* dst_pool, int64_t dst_base, int32_t* new_indices, hipStream_t stream);
+hipError_t launch_tree_accept(const int32_t* parents, const int32_t* draft, const int32_t* target, int B,
+                              int Q, int32_t* accept_len, int32_t* accepted, int32_t* bonus,
+                              hipStream_t stream);
 
 }  // namespace va

@@ -97,3 +97,29 @@ def test_plan_shapes(lib):
     va.set_chunk_override(0)
     with pytest.raises(va.VerifyAttnError):
         va.query_plan(1, 0, 8, 260)
+
+
+def test_kv_defrag_argument_checks(lib):
+    # (src, idx, n, num_slots, dst, dst_base, dst_slots, new_idx, stream): fake but aligned
+    # addresses; every case fails validation before anything touches the device
+    ok = (4096, 4096, 8, 100, 8192, 0, 100, 4096 * 3, None)
+    assert lib.verify_attn_kv_defrag(*ok[:2], 0, *ok[3:]) == va.VA_OK          # n = 0: nothing to do
+    bad = [
+        dict(i=0, v=None), dict(i=4, v=None), dict(i=7, v=None),               # null pointers
+        dict(i=0, v=4100), dict(i=4, v=4104), dict(i=1, v=4098),               # misaligned
+        dict(i=2, v=-1), dict(i=3, v=0), dict(i=6, v=0),                       # bad sizes
+        dict(i=5, v=-1), dict(i=5, v=93), dict(i=6, v=7),                      # run outside the destination
+    ]
+    for case in bad:
+        args = list(ok)
+        args[case["i"]] = case["v"]
+        assert lib.verify_attn_kv_defrag(*args) == va.VA_EINVAL, case
+        assert lib.verify_attn_last_error()
+
+
+def test_tree_accept_argument_checks(lib):
+    ok = [4096, 4096, 4096, 2, 8, 8192, 8192, 8192, None]
+    for i, v in ((3, 0), (4, 0), (4, 65), (0, None), (5, None), (7, None), (1, 4098), (6, 4097)):
+        args = list(ok)
+        args[i] = v
+        assert lib.verify_attn_tree_accept(*args) == va.VA_EINVAL, (i, v)
