@@ -120,6 +120,115 @@ def cpu_baseline(w, heads, min_seconds=10.0, max_reps=20):
     }
 
 
+def _event_times(torch, fn, steps, flush=None):
+    """Mean and median µs of `fn` over `steps` calls timed with HIP events on the
+    current stream (each preceded by a cache-evicting fill when `flush` is given)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        if flush is not None:
+            flush.zero_()
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    t = np.array([e0.elapsed_time(e1) for e0, e1 in ev]) * 1e3
+    return float(t.mean()), float(np.median(t))
+
+
+def bench_defrag(args, torch, va) -> int:
+    """KV defragmentation of the 185k-prefix workload's 185,016 positions into a
+    contiguous run: µs/call and algorithmic HBM GB/s (row read + row write + index
+    read + index write per position) against 8 TB/s; the oracle as CPU baseline."""
+    from workloads import make_config
+    w = make_config(args.config)
+    dev = torch.device("cuda:0")
+    src = torch.from_numpy(w.kv_pool.view(np.int16)).to(dev)
+    idx = torch.from_numpy(w.kv_indices).to(dev)
+    n = int(w.total_kv)
+    dst = torch.empty((n, 576), dtype=torch.int16, device=dev)
+    new_idx = torch.empty(n, dtype=torch.int32, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def call():
+        va.kv_defrag(src, idx, dst, 0, new_indices=new_idx)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    cold, cold_med = _event_times(torch, call, args.steps, flush)
+    warm, _ = _event_times(torch, call, args.steps)
+    nbytes = n * (2 * 1152 + 8)
+    res = {
+        "metric": "kv-defrag µs/call + achieved HBM GB/s (% of peak)", "value": round(cold, 2), "unit": "µs/call",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(cold / 1e3, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": f"{args.config}: {n} positions, pool rows of 1152 B, shuffled slots, "
+                               "copied into a contiguous run", "cache_flush_between_calls": True},
+        "us_per_call_median": round(cold_med, 2), "us_per_call_warm": round(warm, 2),
+        "algorithmic_bytes": nbytes,
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / (cold * 1e-6) / 1e9, 1), "peak": PEAK_HBM / 1e9,
+                     "unit": "GB/s", "frac": round(nbytes / (cold * 1e-6) / PEAK_HBM, 4), "traffic": None,
+                     "kernel": "defrag_kernel"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        reps = 0
+        while reps == 0 or time.perf_counter() - t0 < 5.0:
+            oracle.defrag(w.kv_pool, w.kv_indices, np.zeros((n, 576), np.uint16), 0)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        res["cpu_baseline"] = {"value": round(dt * 1e6, 1), "unit": "µs/call", "cores": 1, "kind": "oracle",
+                               "sample": f"oracle.defrag on all {n} positions, {reps} calls, {dt:.2f} s each"}
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def bench_tree_accept(args, torch, va) -> int:
+    """Greedy acceptance over 256 draft trees of 64 nodes (depth <= 8): µs/call
+    (launch-latency bound); the oracle as CPU baseline."""
+    from workloads import make_tree_accept_case
+    B, Q = 256, 64
+    par, dr, tg = make_tree_accept_case(700, B, Q, vocab=8, p_follow=0.9)
+    dev = torch.device("cuda:0")
+    ins = [torch.from_numpy(a).to(dev) for a in (par, dr, tg)]
+    out = va.tree_accept(*ins)
+
+    def call():
+        va.tree_accept(*ins, out=out)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    mean, med = _event_times(torch, call, args.steps)
+    res = {
+        "metric": "tree-accept µs/call", "value": round(mean, 2), "unit": "µs/call", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(mean / 1e3, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": f"B={B} draft trees of Q={Q} nodes, depth <= 8, vocabulary 8, target follows a "
+                               "child with p=0.9"},
+        "us_per_call_median": round(med, 2),
+        "roofline": {"bound": "latency", "achieved": None, "peak": None, "unit": None, "frac": None,
+                     "traffic": None, "kernel": "tree_accept_kernel"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        reps = 0
+        while reps == 0 or time.perf_counter() - t0 < 2.0:
+            oracle.tree_accept_batch(par, dr, tg)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        res["cpu_baseline"] = {"value": round(dt * 1e6, 1), "unit": "µs/call", "cores": 1, "kind": "oracle",
+                               "sample": f"oracle.tree_accept_batch on the same inputs, {reps} calls"}
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 3) -> None:
     """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE."""
     import torch
@@ -141,6 +250,9 @@ def main() -> int:
     ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting fill between calls")
     ap.add_argument("--chunk", type=int, default=0, help="keys-per-chunk override (0 = automatic)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--op", default="attn", choices=["attn", "defrag", "tree_accept"],
+                    help="attn (default): the verify-attention call; defrag / tree_accept: the steps next "
+                         "to it, each with its own metric line")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -159,6 +271,10 @@ def main() -> int:
 
     import speculative_decoding_verify_03_amd as va
     from workloads import make_config
+    if args.op == "defrag":
+        return bench_defrag(args, torch, va)
+    if args.op == "tree_accept":
+        return bench_tree_accept(args, torch, va)
 
     print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
     w = make_config(args.config)
