@@ -12,7 +12,8 @@
 // gfx950 mapping, per workgroup (8 waves, two per SIMD, 128 query-head rows):
 //  * gather: every 32-key tile is brought into LDS with 16-byte direct
 //    global->LDS loads through kv_indices (page_size 1, 1152-byte rows), one
-//    whole 128-byte line per 8 lanes; a 3-deep ring keeps two tiles in flight;
+//    whole 128-byte line per 8 lanes, all issued by one half of the waves; a
+//    3-slot ring holds the tile being applied, the next one, and one in flight;
 //  * scores: S^T = K Q^T on MFMA 32x32x16 bf16. K comes from LDS (A operand);
 //    each pair of waves keeps its 32 query rows resident in VGPRs (B operand),
 //    split by latent dims. All heads and verify positions of the tile share
@@ -45,7 +46,6 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kChunks = kRowBytes / 16;          // 72 chunk columns per row
 constexpr int kTileBytes = kUnit * kRowBytes;    // 36864 bytes per tile
-constexpr int kRing = 4;                         // tiles resident in LDS
 constexpr int kKSteps = kLatent / 16;            // 36 MFMA k-steps over the latent
 constexpr int kDvBlocks = kValue / 32;           // 16 value blocks of 32 dims
 constexpr float kLog2e = 1.4426950408889634f;
@@ -65,42 +65,38 @@ __device__ __forceinline__ int tile_offset(int chunk, int key) {
   return ((key >> 3) * 9 + (chunk >> 3)) * 1024 + ((key & 7) * 8 + ((chunk & 7) ^ ((key >> 1) & 7))) * 16;
 }
 
-// The gather is line-granular: wave w of the 8 fetches key group w/2 (8 keys)
-// and 128-byte lines [0, 5) (even w) or [5, 9) (odd w) of each of those rows;
-// lane l reads key 8(w/2) + l/8 and the 16-byte chunk of the line that lands in
-// slot l of the region. Every load instruction thus fetches 8 whole lines.
+// The gather is line-granular and done by four waves: gathering wave j fetches
+// key group j (8 keys), all nine 128-byte lines of each of those rows; lane l
+// reads key 8j + l/8 and, of every line, the 16-byte chunk that lands in slot l
+// of the line's region. Every load instruction thus fetches 8 whole lines.
+constexpr int kGatherWaves = kUnit / 8;
+constexpr int kGatherLoads = kRowBytes / 128;   // 9 load instructions per wave and tile
+
 struct GatherLane {
   int key;   // key of the tile this lane fetches
   int coff;  // byte offset of its chunk inside a 128-byte line
   int kg;    // key group (region row)
-  int L0;    // first line
-  int nld;   // number of lines (5 or 4)
 };
 
-__device__ __forceinline__ GatherLane gather_lane(int wave, int lane) {
+__device__ __forceinline__ GatherLane gather_lane(int gw, int lane) {
   GatherLane g;
-  g.kg = wave >> 1;
-  g.key = 8 * g.kg + (lane >> 3);
+  g.kg = gw;
+  g.key = 8 * gw + (lane >> 3);
   g.coff = ((lane & 7) ^ ((g.key >> 1) & 7)) * 16;
-  g.L0 = (wave & 1) ? 5 : 0;
-  g.nld = (wave & 1) ? 4 : 5;
   return g;
 }
 
-// Issue this wave's share of one tile gather. `slot` is the pool row of the
-// lane's key (any out-of-range value for an absent position: zero row).
+// Issue this wave's share of one tile gather (exactly kGatherLoads load
+// instructions). `slot` is the pool row of the lane's key (any out-of-range
+// value for an absent position: zero row).
 __device__ __forceinline__ void issue_tile_gather(const char* kv_pool, int64_t num_slots, int32_t slot,
                                                   LDS_AS char* tile, const GatherLane& gl) {
   const char* row = (slot >= 0 && slot < num_slots) ? kv_pool + (int64_t)slot * kRowBytes
                                                     : reinterpret_cast<const char*>(g_zero_row);
   row += gl.coff;
 #pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    if (i < gl.nld) {
-      const int L = gl.L0 + i;
-      __builtin_amdgcn_global_load_lds(row + L * 128, tile + (gl.kg * 9 + L) * 1024, 16, 0, 0);
-    }
-  }
+  for (int L = 0; L < kGatherLoads; ++L)
+    __builtin_amdgcn_global_load_lds(row + L * 128, tile + (gl.kg * 9 + L) * 1024, 16, 0, 0);
 }
 
 __device__ __forceinline__ LDS_AS char* lds_cast(char* p) { return (LDS_AS char*)(p); }
@@ -218,14 +214,20 @@ constexpr int kOffP = kOffXchg + kPairs * kXchgBytes;              // 126976
 constexpr int kOffAlpha = kOffP + 2 * kPairs * kPBytes;            // 143360: P, two tile parities
 constexpr int kOffFlag = kOffAlpha + 2 * kRowsPerWG * 4;           // 144384: rescale factors, two parities
 constexpr int kOffSlots = kOffFlag + 64;                           // 144448: slot-index ring
-constexpr int kSlotRing = 6;                                       // 256 bytes per tile
-constexpr int kSlotAhead = 5;                                      // slot copy distance, tiles
-constexpr int kPrefAhead = 4;                                      // L2 prefetch distance, tiles
-constexpr int kOffPref = kOffSlots + kSlotRing * 256;              // 145984: prefetch sink
-constexpr int kOffQPark = kOffPref + 256;                          // 146240
-constexpr int kSplitLds = kOffQPark + kSplitWaves * kQParkBytes;   // 162624
+constexpr int kSlotRing = 8;                                       // 256 bytes per tile
+constexpr int kGatherAhead = 3;                                    // tile u+3 is gathered while tile u is applied
+constexpr int kSlotAhead = 7;                                      // slot copy distance, tiles
+constexpr int kPrefAhead = 5;                                      // L2 prefetch distance, tiles
+constexpr int kOffPref = kOffSlots + kSlotRing * 256;              // 146496: prefetch sink
+constexpr int kOffQPark = kOffPref + 256;                          // 146752
+constexpr int kSplitLds = kOffQPark + kSplitWaves * kQParkBytes;   // 163136
 static_assert(kSplitLds <= 160 * 1024, "split kernel LDS budget");
-static_assert(kSlotRing > kSlotAhead && kSlotAhead > kPrefAhead && kPrefAhead > 2, "slot ring distances");
+// A slot copy issued in phase X of iteration v lands before the barrier that
+// ends phase X of iteration v+1; gathers read it kGatherAhead and prefetches
+// kPrefAhead tiles ahead of their tile.
+static_assert(kSlotAhead - 2 >= kGatherAhead && kSlotAhead - 2 >= kPrefAhead && kPrefAhead > kGatherAhead,
+              "slot copy distances");
+static_assert(kSlotRing > kSlotAhead && kGatherAhead == kRingS, "ring sizes");
 
 template <int V>
 struct IntC {
@@ -329,22 +331,23 @@ split_kernel(SplitArgs a) {
   LDS_AS char* abuf = lds + kOffAlpha;
   LDS_AS char* fbuf = lds + kOffFlag;
 
-  // Gather bookkeeping (see gather_lane): even waves issue 5 loads per tile,
-  // odd waves 4; lane l always fetches the same key of a tile.
+  // Gather bookkeeping (see gather_lane): the odd half (waves 4-7) issues all
+  // direct-to-LDS loads, nine per wave and tile; lane l always fetches the
+  // same key of a tile. The even half issues none inside the loop, so its
+  // LDS reads never wait on them.
   // (The per-lane gather fields are re-derived from fresh_lane() at each use,
   // so they do not occupy registers across the loop.)
-  auto glane = [&]() { return gather_lane(wave, fresh_lane()); };
-  // Slot indices travel through LDS like the latent rows: wave 0 copies the
-  // 32 kv_indices entries of tile v into ring entry v % 6 with one
-  // direct-to-LDS dword load (lanes 32-63 duplicate lanes 0-31), three tiles
-  // before the gather that needs them and one before the L2 prefetch, so the
-  // loop-top vmcnt wait covers them too. (A register load would make the
-  // compiler wait for it with a vmcnt that also drains the gathers issued
-  // after it.)
+  auto glane = [&]() { return gather_lane(wave - 4, fresh_lane()); };
+  // Slot indices travel through LDS like the latent rows: wave 4 copies the
+  // 32 kv_indices entries of tile v into ring entry v % 8 with one
+  // direct-to-LDS dword load (lanes 32-63 duplicate lanes 0-31), kSlotAhead
+  // tiles ahead, so that the vmcnt waits that cover the gathers cover them
+  // too. (A register load would make the compiler wait for it with a vmcnt
+  // that also drains the gathers issued after it.)
   LDS_AS char* slot_ring = lds + kOffSlots;
   auto tile_key_ok = [&](int v, int gkey) -> bool { return kstart + (int64_t)v * kUnit + gkey < kend; };
   auto load_slots_to_lds = [&](int v) {
-    if (wave == 0) {
+    if (wave == 4) {
       int64_t gpos = sbase + kstart + (int64_t)v * kUnit + (lane & 31);
       gpos = gpos < a.total_kv ? gpos : a.total_kv - 1;
       gpos = gpos < 0 ? 0 : gpos;
@@ -366,8 +369,7 @@ split_kernel(SplitArgs a) {
   // rt + row_tiles * m of tile v's 288 lines (9 per key), so the row tiles of
   // a chunk, which run side by side on one XCD, bring each line into L2 once
   // between them, ahead of the gathers. Always exactly one instruction (lanes
-  // without a line read the zero row), which keeps the loop-top vmcnt
-  // counts exact.
+  // without a line read the zero row), which keeps the vmcnt counts exact.
   auto prefetch = [&](int v, bool live) {
     const int fl = fresh_lane();
     const int m = (wave - 4) * 64 + fl;
@@ -411,230 +413,255 @@ split_kernel(SplitArgs a) {
   };
   // O^T += V(v)^T P(v)^T for this wave's 64 dims and all 128 rows.
   auto apply_values = [&](int v, const f16x8 (&va)[kWaveDvBlocks][2]) {
+    // P operands are read one row block ahead of their MFMAs
+    f16x8 pb[2][2];
+    auto pload = [&](int rb, f16x8 (&d)[2]) {
+      d[0] = *reinterpret_cast<LDS_AS const f16x8*>(pbuf_of(v) + rb * kPBytes);
+      d[1] = *reinterpret_cast<LDS_AS const f16x8*>(pbuf_of(v) + rb * kPBytes + 1024);
+    };
+    pload(0, pb[0]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb) {
-      const f16x8 pb0 = *reinterpret_cast<LDS_AS const f16x8*>(pbuf_of(v) + rb * kPBytes);
-      const f16x8 pb1 = *reinterpret_cast<LDS_AS const f16x8*>(pbuf_of(v) + rb * kPBytes + 1024);
+      if (rb + 1 < kRowBlocks) pload(rb + 1, pb[(rb + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
       // key step outer, so consecutive MFMAs are independent
 #pragma unroll
       for (int db = 0; db < kWaveDvBlocks; ++db)
-        o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[db][0], pb0, o[rb][db], 0, 0, 0);
+        o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[db][0], pb[rb & 1][0], o[rb][db], 0, 0, 0);
 #pragma unroll
       for (int db = 0; db < kWaveDvBlocks; ++db)
-        o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[db][1], pb1, o[rb][db], 0, 0, 0);
+        o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[db][1], pb[rb & 1][1], o[rb][db], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // One half's pipeline (PP = p). The even half computes its share of the
-  // scores of tile u, runs the softmax, and applies tile u after the second
-  // barrier. The odd half computes its share of the scores, then applies
-  // tile u-1 while the even half runs the softmax of tile u (keeping the
-  // matrix cores busy), and reads the values of tile u for the next
-  // iteration. Both copies execute the same barriers.
+  // ---- partial scores S^T of one tile over this wave's 288 dims. The K
+  // operands (and parked queries) are read kDepth k-steps ahead of their MFMA;
+  // the scheduling barriers keep the compiler from sinking each read next to
+  // its use, which would expose one LDS round trip per MFMA.
+  auto scores = [&](LDS_AS const char* tile) -> f32x16 {
+    f32x16 acc = f32x16{};
+    int a_off[4];
+    score_offsets(a_off);
+    constexpr int kDepth = 4;    // K reads in flight
+    constexpr int kQDepth = 2;   // parked-query reads in flight
+    auto kload = [&](int ks) {
+      return *reinterpret_cast<LDS_AS const bf16x8*>(tile + a_off[ks & 3] + (ks >> 2) * 1024);
+    };
+    auto qpark = [&](int ks) {
+      return *reinterpret_cast<LDS_AS const bf16x8*>(my_q + (ks - kRegKSteps) * 1024);
+    };
+    bf16x8 kb[kDepth], qb[kQDepth];
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) kb[i] = kload(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < kHalfKSteps; ++ks) {
+      const bf16x8 kc = kb[ks % kDepth];
+      const bf16x8 qc = ks < kRegKSteps ? qf[ks < kRegKSteps ? ks : 0] : qb[ks % kQDepth];
+      if (ks + kDepth < kHalfKSteps) kb[ks % kDepth] = kload(ks + kDepth);
+      if (ks + kQDepth >= kRegKSteps && ks + kQDepth < kHalfKSteps) qb[ks % kQDepth] = qpark(ks + kQDepth);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qc, acc, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return acc;
+  };
+  // The odd half hands its partial block to the even half of its pair.
+  auto write_xchg = [&](const f32x16& sa) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      *reinterpret_cast<LDS_AS f32x4*>(xchg + k * 1024) = f32x4{sa[4 * k], sa[4 * k + 1], sa[4 * k + 2], sa[4 * k + 3]};
+  };
+  // ---- even half: full scores of tile u, mask, running max, lazy rescale,
+  // probabilities; publishes P(u), the rescale factors and the rescale flag.
+  auto softmax = [&](int u, const f32x16& sa) {
+    float x[16];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f32x4 d = *reinterpret_cast<LDS_AS const f32x4*>(xchg + k * 1024);
+      x[4 * k] = (sa[4 * k] + d[0]) * a.c_log2;
+      x[4 * k + 1] = (sa[4 * k + 1] + d[1]) * a.c_log2;
+      x[4 * k + 2] = (sa[4 * k + 2] + d[2]) * a.c_log2;
+      x[4 * k + 3] = (sa[4 * k + 3] + d[3]) * a.c_log2;
+    }
+    const int64_t ustart = kstart + (int64_t)u * kUnit;
+    if (ustart + kUnit > P || ustart + kUnit > kend) {
+      // Positions relative to the tile start fit in 32 bits (a chunk is at
+      // most 2^31 keys). Branch-free selects: a short-circuit form of this
+      // test was compiled into control flow that dropped the -inf store for
+      // hidden tail keys.
+      const int rel0 = (int)(ustart - P);
+      const int end0 = (int)(kend - ustart);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kk = 16 * (i >> 3) + 8 * h + (i & 7);
+        const int rel = rel0 + kk;
+        const unsigned tail_bit = (unsigned)(tbits >> (unsigned)(rel & 63)) & 1u;
+        const unsigned vis = (unsigned)(kk < end0) & ((unsigned)(rel < 0) | tail_bit);
+        x[i] = vis ? x[i] : -INFINITY;
+      }
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
+    mx = fmaxf(mx, swap_halves(mx));
+    const bool grow = mx > m_ref + kLazyRescale;  // false while the row has seen nothing
+    const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.f;  // exp2(-inf) = 0
+    if (grow) m_ref = mx;
+    l_sum *= alpha;
+    const float mref_safe = m_ref == -INFINITY ? 0.f : m_ref;
+    f16x8 p0, p1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float e0 = __builtin_amdgcn_exp2f(x[j] - mref_safe);
+      const float e1 = __builtin_amdgcn_exp2f(x[8 + j] - mref_safe);
+      l_sum += e0 + e1;
+      p0[j] = (_Float16)e0;
+      p1[j] = (_Float16)e1;
+    }
+    *reinterpret_cast<LDS_AS f16x8*>(pbuf_of(u) + pair * kPBytes) = p0;
+    *reinterpret_cast<LDS_AS f16x8*>(pbuf_of(u) + pair * kPBytes + 1024) = p1;
+    const int any_grow = __ballot(grow) != 0;  // wave-wide: taken before any lane is masked off
+    if (h == 0) *reinterpret_cast<LDS_AS float*>(abuf_of(u) + (pair * 32 + n) * 4) = alpha;
+    if (lane == 0) *reinterpret_cast<LDS_AS int*>(fbuf_of(u) + pair * 4) = any_grow;
+  };
+  // ---- this wave's value operands of one tile: V^T for its two 32-dim
+  // blocks and both 16-key steps, transposed and converted to fp16.
+  // The eight transpose reads and their wait form one asm statement, so the
+  // outputs are complete when it ends. (As separate builtins the compiler
+  // fences each with vmcnt(0) against the direct-to-LDS loads in flight, which
+  // would drain the gathers; split into an asm read plus a later wait, the
+  // compiler may copy a destination register before the data has arrived.)
+  // The leading s_nop keeps the new register writes clear of operand reads of
+  // MFMAs still in flight.
+  auto read_values = [&](LDS_AS const char* tile, f16x8 (&va)[kWaveDvBlocks][2]) {
+    u32x2 v[kWaveDvBlocks][2][2];   // [d][t][hf]
+    int tr_off[2][2];
+    value_offsets(tr_off);
+    const unsigned a00 = (unsigned)(uintptr_t)(tile + tr_off[0][0]);
+    const unsigned a10 = (unsigned)(uintptr_t)(tile + tr_off[1][0]);
+    const unsigned a01 = (unsigned)(uintptr_t)(tile + tr_off[0][1]);
+    const unsigned a11 = (unsigned)(uintptr_t)(tile + tr_off[1][1]);
+    asm volatile(
+        "s_nop 7\n\t"
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:18432\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:18432\n\t"
+        "ds_read_b64_tr_b16 %4, %10\n\t"
+        "ds_read_b64_tr_b16 %5, %11\n\t"
+        "ds_read_b64_tr_b16 %6, %10 offset:18432\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:18432\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0][0][0]), "=&v"(v[0][0][1]), "=&v"(v[0][1][0]), "=&v"(v[0][1][1]),
+          "=&v"(v[1][0][0]), "=&v"(v[1][0][1]), "=&v"(v[1][1][0]), "=&v"(v[1][1][1])
+        : "v"(a00), "v"(a10), "v"(a01), "v"(a11)
+        : "memory");
+#pragma unroll
+    for (int db = 0; db < kWaveDvBlocks; ++db)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        bf16x4_to_f16(v[db][t][0], va[db][t], 0);
+        bf16x4_to_f16(v[db][t][1], va[db][t], 4);
+      }
+  };
+
+  // One half's pipeline (PP = p). Each iteration u has two phases, each
+  // closed by a barrier, and the two waves of a SIMD take turns on its matrix
+  // core:
+  //   phase Y: the even wave runs the softmax of tile u (vector ALU) while the
+  //            odd wave applies tile u-1 to its values and computes its
+  //            partial scores of tile u+1 (34 MFMAs); both then read their
+  //            value operands of tile u, which frees tile u's ring slot;
+  //   phase X: the even wave applies tile u and computes its partial scores
+  //            of tile u+1 (34 MFMAs) while the odd wave hands over its
+  //            partial scores, issues the gather of tile u+3 into the freed
+  //            slot and the prefetches, and waits for tile u+2.
+  // P, the rescale factors and flags are double-buffered by tile parity, as
+  // the odd half reads those of tile u-1 while the even half writes tile u's.
   auto run = [&](auto pc) {
     constexpr int PP = decltype(pc)::value;
+    if (nunits == 0) return;   // uniform across the workgroup
 
-    // Prologue, in the same order as the loop body: [slots][tile u+2][prefetch]
-    // (the prologue's two prefetches touch nothing; they keep the counts).
-    {
+    // Prologue: gathers of tiles 0-2, slot copies of tiles 3..kSlotAhead-1,
+    // and one prefetch that touches nothing, in the order that gives the loop
+    // its vmcnt counts; then wait for everything but tile 2.
+    if constexpr (PP == 1) {
       const int32_t s0 = load_slot(0);
       const int32_t s1 = load_slot(1);
+      const int32_t s2 = load_slot(2);
       issue(s0, lds);
-      for (int v = 2; v < kSlotAhead; ++v) load_slots_to_lds(v);
-      if constexpr (PP == 1) prefetch(0, false);
       issue(s1, lds + kTileBytes);
-      if constexpr (PP == 1) prefetch(0, false);
+      for (int v = kGatherAhead; v < kSlotAhead; ++v) load_slots_to_lds(v);
+      issue(s2, lds + 2 * kTileBytes);
+      prefetch(0, false);
+      asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
     }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    f32x16 sa = scores(lds);   // tile 0, both halves
+    if constexpr (PP == 1) write_xchg(sa);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
     f16x8 vheld[kWaveDvBlocks][2];   // odd half: values of the previous tile
 #pragma unroll
     for (int db = 0; db < kWaveDvBlocks; ++db) vheld[db][0] = vheld[db][1] = f16x8{};
 
     for (int u = 0; u < nunits; ++u) {
-      // Since tile u went out, this wave issued the 5 or 4 loads of tile u+1
-      // (wave 0 also the slot copy of tile u+4, before them; the odd half
-      // also one prefetch after each of the last two gathers). Once no more
-      // than those are outstanding, tile u and the slots of tile u+4 have
-      // landed (the compiler does not track direct-to-LDS loads, so this wait
-      // is explicit). The barrier is issued by hand so that it does not also
-      // drain the next tile's loads. It also guarantees that every wave is
-      // done with tile u-1 (the odd half holds its values in registers).
-      if constexpr (PP == 0) {
-        if ((wave & 1) == 0) asm volatile("s_waitcnt vmcnt(5)\n\ts_barrier" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
-      } else {
-        if ((wave & 1) == 0) asm volatile("s_waitcnt vmcnt(7)\n\ts_barrier" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
-      }
-
       LDS_AS char* tile = lds + (u % kRingS) * kTileBytes;
-      const int32_t slot_u2 = read_slot(u + 2);
-      load_slots_to_lds(u + kSlotAhead);
-      issue(slot_u2, lds + ((u + 2) % kRingS) * kTileBytes);  // tile u-1's slot is free
+      LDS_AS char* next = lds + ((u + 1) % kRingS) * kTileBytes;
+      const bool more = u + 1 < nunits;
 
-      // ---- partial scores S^T over this wave's 288 dims. The K operands (and
-      // parked queries) are read kDepth k-steps ahead of their MFMA; the
-      // scheduling barriers keep the compiler from sinking each read next to
-      // its use, which would expose one LDS round trip per MFMA.
-      f32x16 sa = f32x16{};
-      {
-        int a_off[4];
-        score_offsets(a_off);
-        constexpr int kDepth = 3;    // K reads in flight
-        constexpr int kQDepth = 2;   // parked-query reads in flight
-        auto kload = [&](int ks) {
-          return *reinterpret_cast<LDS_AS const bf16x8*>(tile + a_off[ks & 3] + (ks >> 2) * 1024);
-        };
-        auto qpark = [&](int ks) {
-          return *reinterpret_cast<LDS_AS const bf16x8*>(my_q + (ks - kRegKSteps) * 1024);
-        };
-        bf16x8 kb[kDepth], qb[kQDepth];
-#pragma unroll
-        for (int i = 0; i < kDepth; ++i) kb[i] = kload(i);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ks = 0; ks < kHalfKSteps; ++ks) {
-          const bf16x8 kc = kb[ks % kDepth];
-          const bf16x8 qc = ks < kRegKSteps ? qf[ks < kRegKSteps ? ks : 0] : qb[ks % kQDepth];
-          if (ks + kDepth < kHalfKSteps) kb[ks % kDepth] = kload(ks + kDepth);
-          if (ks + kQDepth >= kRegKSteps && ks + kQDepth < kHalfKSteps) qb[ks % kQDepth] = qpark(ks + kQDepth);
-          sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qc, sa, 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      if constexpr (PP == 1) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          *reinterpret_cast<LDS_AS f32x4*>(xchg + k * 1024) =
-              f32x4{sa[4 * k], sa[4 * k + 1], sa[4 * k + 2], sa[4 * k + 3]};
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-
-      if constexpr (PP == 1) {
-        // ---- while the even half runs the softmax: prefetch, then apply the
-        // previous tile
-        prefetch(u + kPrefAhead, true);
+      // ---- phase Y
+      if constexpr (PP == 0) {
+        softmax(u, sa);
+      } else {
         if (u > 0) {
           rescale(u - 1);
           apply_values(u - 1, vheld);
         }
-      } else {
-        // ---- full scores, mask, running max, lazy rescale, probabilities
-        float x[16];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const f32x4 d = *reinterpret_cast<LDS_AS const f32x4*>(xchg + k * 1024);
-          x[4 * k] = (sa[4 * k] + d[0]) * a.c_log2;
-          x[4 * k + 1] = (sa[4 * k + 1] + d[1]) * a.c_log2;
-          x[4 * k + 2] = (sa[4 * k + 2] + d[2]) * a.c_log2;
-          x[4 * k + 3] = (sa[4 * k + 3] + d[3]) * a.c_log2;
-        }
-        const int64_t ustart = kstart + (int64_t)u * kUnit;
-        if (ustart + kUnit > P || ustart + kUnit > kend) {
-          // Positions relative to the tile start fit in 32 bits (a chunk is
-          // at most 2^31 keys). Branch-free selects: a short-circuit form of
-          // this test was compiled into control flow that dropped the -inf
-          // store for hidden tail keys.
-          const int rel0 = (int)(ustart - P);
-          const int end0 = (int)(kend - ustart);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kk = 16 * (i >> 3) + 8 * h + (i & 7);
-            const int rel = rel0 + kk;
-            const unsigned tail_bit = (unsigned)(tbits >> (unsigned)(rel & 63)) & 1u;
-            const unsigned vis = (unsigned)(kk < end0) & ((unsigned)(rel < 0) | tail_bit);
-            x[i] = vis ? x[i] : -INFINITY;
-          }
-        }
-        float mx = x[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
-        mx = fmaxf(mx, swap_halves(mx));
-        const bool grow = mx > m_ref + kLazyRescale;  // false while the row has seen nothing
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.f;  // exp2(-inf) = 0
-        if (grow) m_ref = mx;
-        l_sum *= alpha;
-        const float mref_safe = m_ref == -INFINITY ? 0.f : m_ref;
-        f16x8 p0, p1;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float e0 = __builtin_amdgcn_exp2f(x[j] - mref_safe);
-          const float e1 = __builtin_amdgcn_exp2f(x[8 + j] - mref_safe);
-          l_sum += e0 + e1;
-          p0[j] = (_Float16)e0;
-          p1[j] = (_Float16)e1;
-        }
-        *reinterpret_cast<LDS_AS f16x8*>(pbuf_of(u) + pair * kPBytes) = p0;
-        *reinterpret_cast<LDS_AS f16x8*>(pbuf_of(u) + pair * kPBytes + 1024) = p1;
-        const int any_grow = __ballot(grow) != 0;  // wave-wide: taken before any lane is masked off
-        if (h == 0) *reinterpret_cast<LDS_AS float*>(abuf_of(u) + (pair * 32 + n) * 4) = alpha;
-        if (lane == 0) *reinterpret_cast<LDS_AS int*>(fbuf_of(u) + pair * 4) = any_grow;
+        // (the else branch keeps the old block from living on through the MFMAs)
+        if (more) sa = scores(next);
+        else sa = f32x16{};
       }
-
-      // ---- this wave's value operands of tile u: V^T for its two 32-dim
-      // blocks and both 16-key steps, transposed and converted to fp16
       f16x8 va[kWaveDvBlocks][2];
-      {
-        // The eight transpose reads and their wait form one asm statement, so
-        // the outputs are complete when it ends. (As separate builtins the
-        // compiler fences each with vmcnt(0) against the direct-to-LDS loads
-        // in flight, which would drain the gather prefetch; split into an asm
-        // read plus a later wait, the compiler may copy a destination register
-        // before the data has arrived.) The leading s_nop keeps the new
-        // register writes clear of operand reads of MFMAs still in flight.
-        u32x2 v[kWaveDvBlocks][2][2];   // [d][t][hf]
-        {
-          int tr_off[2][2];
-          value_offsets(tr_off);
-          const unsigned a00 = (unsigned)(uintptr_t)(tile + tr_off[0][0]);
-          const unsigned a10 = (unsigned)(uintptr_t)(tile + tr_off[1][0]);
-          const unsigned a01 = (unsigned)(uintptr_t)(tile + tr_off[0][1]);
-          const unsigned a11 = (unsigned)(uintptr_t)(tile + tr_off[1][1]);
-          asm volatile(
-              "s_nop 7\n\t"
-              "ds_read_b64_tr_b16 %0, %8\n\t"
-              "ds_read_b64_tr_b16 %1, %9\n\t"
-              "ds_read_b64_tr_b16 %2, %8 offset:18432\n\t"
-              "ds_read_b64_tr_b16 %3, %9 offset:18432\n\t"
-              "ds_read_b64_tr_b16 %4, %10\n\t"
-              "ds_read_b64_tr_b16 %5, %11\n\t"
-              "ds_read_b64_tr_b16 %6, %10 offset:18432\n\t"
-              "ds_read_b64_tr_b16 %7, %11 offset:18432\n\t"
-              "s_waitcnt lgkmcnt(0)"
-              : "=&v"(v[0][0][0]), "=&v"(v[0][0][1]), "=&v"(v[0][1][0]), "=&v"(v[0][1][1]),
-                "=&v"(v[1][0][0]), "=&v"(v[1][0][1]), "=&v"(v[1][1][0]), "=&v"(v[1][1][1])
-              : "v"(a00), "v"(a10), "v"(a01), "v"(a11)
-              : "memory");
-        }
-        // all LDS stores of this iteration (P/alpha/flag of the even half)
-        // are complete before the barrier
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-#pragma unroll
-        for (int db = 0; db < kWaveDvBlocks; ++db)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            bf16x4_to_f16(v[db][t][0], va[db][t], 0);
-            bf16x4_to_f16(v[db][t][1], va[db][t], 4);
-          }
-      }
+      read_values(tile, va);
+      // P/alpha/flag stores of the even half are complete before the barrier
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
+      // ---- phase X
       if constexpr (PP == 0) {
         rescale(u);
         apply_values(u, va);
+        // Unconditional (after the last tile this reads a landed tile of zero
+        // rows and the result is dropped): a conditional update keeps the old
+        // block live through the MFMAs, and the registers do not allow it.
+        sa = scores(next);
+        asm volatile("s_barrier" ::: "memory");
       } else {
 #pragma unroll
         for (int db = 0; db < kWaveDvBlocks; ++db) {
           vheld[db][0] = va[db][0];
           vheld[db][1] = va[db][1];
         }
+        if (more) write_xchg(sa);
+        load_slots_to_lds(u + kSlotAhead);
+        const int32_t slot = read_slot(u + kGatherAhead);
+        issue(slot, tile);   // nobody reads tile u any more
+        prefetch(u + kPrefAhead, true);
+        // Tile u+2 has landed once no more than the loads issued after it are
+        // outstanding: the prefetch of the previous phase X, this phase's slot
+        // copy (wave 4), nine gather loads and one prefetch. (The compiler
+        // does not track direct-to-LDS loads, so the wait is explicit; the
+        // barrier is issued by hand so that it does not drain tile u+3.)
+        if (wave == 4) asm volatile("s_waitcnt vmcnt(12)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(11)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
       }
     }
     // the odd half's value update of the last tile
     if constexpr (PP == 1) {
-      if (nunits > 0) {
-        rescale(nunits - 1);
-        apply_values(nunits - 1, vheld);
-      }
+      rescale(nunits - 1);
+      apply_values(nunits - 1, vheld);
     }
   };
   if (p == 0) run(IntC<0>{});
@@ -762,10 +789,10 @@ __global__ void __launch_bounds__(256) merge_kernel(const float* __restrict__ pa
 // ---------------------------------------------------------------------------
 // Debug gather: the split kernel's gather routine, copied back out in order.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(512) debug_gather_kernel(const char* __restrict__ kv_pool,
-                                                           const int32_t* __restrict__ kv_indices,
-                                                           int64_t n, int64_t num_slots,
-                                                           u32x4* __restrict__ rows_out) {
+__global__ void __launch_bounds__(kGatherWaves * 64) debug_gather_kernel(const char* __restrict__ kv_pool,
+                                                                         const int32_t* __restrict__ kv_indices,
+                                                                         int64_t n, int64_t num_slots,
+                                                                         u32x4* __restrict__ rows_out) {
   __shared__ __attribute__((aligned(1024))) char smem[kTileBytes];
   LDS_AS char* lds = lds_cast(smem);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -777,7 +804,7 @@ __global__ void __launch_bounds__(512) debug_gather_kernel(const char* __restric
   issue_tile_gather(kv_pool, num_slots, slot, lds, gl);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int p = tid; p < kUnit * kChunks; p += 512) {
+  for (int p = tid; p < kUnit * kChunks; p += kGatherWaves * 64) {
     const int key = p / kChunks, ch = p - key * kChunks;
     if (ustart + key < n)
       rows_out[(ustart + key) * kChunks + ch] =
@@ -813,7 +840,7 @@ hipError_t launch_debug_gather(const void* kv_pool, const int32_t* kv_indices, i
                                int64_t num_slots, void* rows_out, hipStream_t stream) {
   const int64_t tiles = (n + kUnit - 1) / kUnit;
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(debug_gather_kernel, dim3((unsigned)tiles), dim3(512), 0, stream,
+  hipLaunchKernelGGL(debug_gather_kernel, dim3((unsigned)tiles), dim3(kGatherWaves * 64), 0, stream,
                      static_cast<const char*>(kv_pool), kv_indices, n, num_slots,
                      static_cast<u32x4*>(rows_out));
   return hipGetLastError();
