@@ -24,45 +24,54 @@ typedef unsigned u32x4c __attribute__((ext_vector_type(4)));
 
 constexpr int kRowChunks = kRowBytes / 16;   // 72 sixteen-byte chunks per latent row
 constexpr int kDefragThreads = 256;
-constexpr int kDefragPerThread = 4;          // chunks in flight per thread
+constexpr int kDefragRows = 32;              // positions per workgroup
+constexpr int kDefragPerThread = kDefragRows * kRowChunks / kDefragThreads;   // 9 chunks in flight
+static_assert(kDefragRows * kRowChunks % kDefragThreads == 0, "defrag chunk split");
 
 // ---------------------------------------------------------------------------
-// Defragmentation: chunk k of the n * 72 chunks is chunk k % 72 of position
-// k / 72. Consecutive threads take consecutive chunks, so a wave reads and
-// writes whole 1152-byte rows with 16-byte accesses; each thread keeps four
-// loads in flight before its stores. The thread that copies chunk 0 of a
-// position also writes its new index.
+// Defragmentation: one workgroup copies 32 positions. Their 32 slot indices
+// are read once (one coalesced load) into LDS, and the new indices written;
+// then chunk t of the workgroup's 32 * 72 chunks is chunk t % 72 of position
+// t / 72, thread i taking chunks i + 256k. Consecutive threads take
+// consecutive chunks, so a wave reads and writes whole 1152-byte rows with
+// 16-byte accesses, and each thread has all nine of its loads in flight
+// before its stores. Source rows and the destination run are touched once,
+// so both go around the caches' normal replacement (nontemporal).
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(kDefragThreads) defrag_kernel(const u32x4c* __restrict__ src,
                                                                 const int32_t* __restrict__ kv_indices,
                                                                 int64_t n, int64_t num_slots,
                                                                 u32x4c* __restrict__ dst, int64_t dst_base,
                                                                 int32_t* __restrict__ new_indices) {
-  const int64_t total = n * kRowChunks;
-  const int64_t base = (int64_t)blockIdx.x * (kDefragThreads * kDefragPerThread) + threadIdx.x;
+  __shared__ int32_t s_slot[kDefragRows];
+  const int64_t row0 = (int64_t)blockIdx.x * kDefragRows;
+  const int tid = threadIdx.x;
+  if (tid < kDefragRows) {
+    const int64_t j = row0 + tid;
+    int32_t slot = -1;
+    if (j < n) {
+      slot = kv_indices[j];
+      new_indices[j] = (int32_t)(dst_base + j);
+    }
+    s_slot[tid] = (slot >= 0 && slot < num_slots) ? slot : -1;
+  }
+  __syncthreads();
   u32x4c v[kDefragPerThread];
-  int64_t k_of[kDefragPerThread];
 #pragma unroll
   for (int i = 0; i < kDefragPerThread; ++i) {
-    const int64_t k = base + (int64_t)i * kDefragThreads;
-    k_of[i] = k;
+    const int t = tid + i * kDefragThreads;
+    const int r = t / kRowChunks;
+    const int c = t - r * kRowChunks;
+    const int32_t slot = s_slot[r];
     v[i] = u32x4c{0, 0, 0, 0};
-    if (k < total) {
-      const int64_t j = k / kRowChunks;
-      const int c = (int)(k - j * kRowChunks);
-      const int32_t slot = kv_indices[j];
-      if (slot >= 0 && slot < num_slots) v[i] = src[(int64_t)slot * kRowChunks + c];
-    }
+    if (row0 + r < n && slot >= 0) v[i] = __builtin_nontemporal_load(&src[(int64_t)slot * kRowChunks + c]);
   }
 #pragma unroll
   for (int i = 0; i < kDefragPerThread; ++i) {
-    const int64_t k = k_of[i];
-    if (k < total) {
-      const int64_t j = k / kRowChunks;
-      const int c = (int)(k - j * kRowChunks);
-      dst[(dst_base + j) * kRowChunks + c] = v[i];
-      if (c == 0) new_indices[j] = (int32_t)(dst_base + j);
-    }
+    const int t = tid + i * kDefragThreads;
+    const int r = t / kRowChunks;
+    const int c = t - r * kRowChunks;
+    if (row0 + r < n) __builtin_nontemporal_store(v[i], &dst[(dst_base + row0 + r) * kRowChunks + c]);
   }
 }
 
@@ -106,8 +115,7 @@ __global__ void __launch_bounds__(64) tree_accept_kernel(const int32_t* __restri
 
 hipError_t launch_defrag(const void* src_pool, const int32_t* kv_indices, int64_t n, int64_t num_slots,
                          void* dst_pool, int64_t dst_base, int32_t* new_indices, hipStream_t stream) {
-  const int64_t per_wg = (int64_t)kDefragThreads * kDefragPerThread;
-  const int64_t grid = (n * kRowChunks + per_wg - 1) / per_wg;
+  const int64_t grid = (n + kDefragRows - 1) / kDefragRows;
   hipLaunchKernelGGL(defrag_kernel, dim3((unsigned)grid), dim3(kDefragThreads), 0, stream,
                      static_cast<const u32x4c*>(src_pool), kv_indices, n, num_slots,
                      static_cast<u32x4c*>(dst_pool), dst_base, new_indices);
