@@ -90,16 +90,14 @@ def test_many_small_chunks_cross_the_tail(env):
     torch, va = env
     w = make_workload("chunks", [302], B=6, Q=12, H=4, prefix_lens=[1000, 1001, 1003, 1005, 20, 0],
                       mask="tree", num_slots=5000)
-    va.set_chunk_override(32)
-    try:
-        _check(env, w, label="chunk32")
-    finally:
-        va.set_chunk_override(0)
-    va.set_chunk_override(96)
-    try:
-        _check(env, w, label="chunk96")
-    finally:
-        va.set_chunk_override(0)
+    # one, two, three and four tiles per chunk: the pipeline's prologue and
+    # drain at every depth of the tile ring
+    for chunk in (32, 64, 96, 128):
+        va.set_chunk_override(chunk)
+        try:
+            _check(env, w, label=f"chunk{chunk}")
+        finally:
+            va.set_chunk_override(0)
 
 
 def test_out_of_range_slots_read_as_zero_rows(env):
