@@ -194,3 +194,36 @@ def test_late_max_growth_rescales_some_rows(env):
             _check(env, w, label=f"growth_chunk{chunk}")
         finally:
             va.set_chunk_override(0)
+
+
+def _sweep_cases(n=24, seed=911):
+    """Seeded random shapes: batch, draft length, heads, ragged prefixes (including
+    empty ones), mask kind and a forced chunk length, so that plans with one to
+    many chunks per sequence and row tiles with padding rows all occur."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        B = int(rng.integers(1, 5))
+        Q = int(rng.integers(1, 17))
+        H = int(rng.integers(1, 25))
+        prefix = [int(x) for x in rng.integers(0, 1500, size=B)]
+        if i % 5 == 0:
+            prefix[0] = 0
+        mask = ["chain", "tree", "none", "identity"][i % 4]
+        chunk = [0, 32, 64, 160][(i // 4) % 4]
+        cases.append((i, B, Q, H, prefix, mask, chunk))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: f"sweep{c[0]}")
+def test_random_shape_sweep(env, case):
+    i, B, Q, H, prefix, mask, chunk = case
+    torch, va = env
+    w = make_workload(f"sweep{i}", [912, i], B=B, Q=Q, H=H, prefix_lens=prefix, mask=mask,
+                      num_slots=sum(prefix) + B * Q + 64)
+    print(f"[parity] sweep{i}: B={B} Q={Q} H={H} prefix={prefix} mask={mask} chunk={chunk}", flush=True)
+    va.set_chunk_override(chunk)
+    try:
+        _check(env, w, label=f"sweep{i}")
+    finally:
+        va.set_chunk_override(0)
