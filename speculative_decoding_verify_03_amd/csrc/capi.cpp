@@ -62,7 +62,7 @@ bool dims_ok(int B, int Q, int H, int64_t total_kv) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // The split plan. Workgroups are (chunk, 128-row tile) pairs and one
-// workgroup fills a compute unit (8 waves, ~156 KiB of LDS), so the batch is
+// workgroup fills a compute unit (8 waves, ~159 KiB of LDS), so the batch is
 // cut into about floor(CUs / row_tiles) chunks of ~equal length; the plan
 // kernel then sizes each sequence's chunks from its own length.
 bool make_plan(int B, int Q, int H, int64_t total_kv, int ncu, va::Plan* p) {

@@ -11,9 +11,9 @@ constexpr int kLatent = 576;           // key width (bf16 elements per latent ro
 constexpr int kValue = 512;            // value width (leading dims of the row)
 constexpr int kRowBytes = kLatent * 2; // 1152 bytes per pool row
 constexpr int kUnit = 32;              // keys per LDS tile
-constexpr int kRowsPerWave = 32;       // query-head rows owned by one wave
-constexpr int kWaves = 4;              // waves per workgroup
-constexpr int kRowsPerWG = kRowsPerWave * kWaves;  // 128 rows per row tile
+constexpr int kRowsPerBlock = 32;      // query-head rows of one 32x32 MFMA score block
+constexpr int kRowBlocksPerWG = 4;     // score blocks per workgroup (one per wave pair)
+constexpr int kRowsPerWG = kRowsPerBlock * kRowBlocksPerWG;  // 128 rows per row tile
 constexpr int kMinChunk = 256;         // smallest chunk worth a workgroup (keys)
 
 // Host-side split plan (the device refines chunk sizes per sequence).
