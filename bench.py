@@ -45,6 +45,8 @@ WORKLOAD_TEXT = {
     "tree32k": "B=1 H=64 Q=16 prefix=32768 random draft tree (depth<=8), 262144-slot pool, shuffled",
     "batch8": "B=8 H=64 Q=8 prefixes U[1024,131072], random draft trees, 2097152-slot pool, shuffled",
     "tiny": "B=1 H=8 Q=4 prefix=256 causal chain, 1024-slot pool, shuffled",
+    "long185k_contig": "long185k over a defragmented cache: contiguous kv_indices (arange), 185016-slot pool",
+    "long185k_h8_contig": "long185k_h8 over a defragmented cache: contiguous kv_indices (arange), 185016-slot pool",
 }
 
 

@@ -227,3 +227,15 @@ def test_random_shape_sweep(env, case):
         _check(env, w, label=f"sweep{i}")
     finally:
         va.set_chunk_override(0)
+
+
+def test_defragmented_cache_full_size_bitwise_equal(env):
+    """The 8-head 185k workload over a shuffled pool and over the same rows laid out
+    contiguously (what KV defragmentation produces): same q, same rows, only the
+    slots differ, so the output must be identical bit for bit."""
+    torch, va = env
+    w1, w2 = make_config("long185k_h8"), make_config("long185k_h8_contig")
+    assert np.array_equal(w1.kv_pool[w1.kv_indices], w2.kv_pool[w2.kv_indices])
+    o1, l1 = run_gpu(va, upload(w1), w1.scale)
+    o2, l2 = run_gpu(va, upload(w2), w2.scale)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)

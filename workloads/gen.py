@@ -201,6 +201,11 @@ CONFIGS: Dict[str, dict] = {
                    num_slots=2097152),
     "long185k_h8": dict(seed=6, B=1, Q=16, H=8, prefix_lens=[185000], mask="chain",
                         num_slots=524288, q_scale=0.5),
+    # The same two shapes over a defragmented cache (contiguous kv_indices).
+    "long185k_contig": dict(seed=4, B=1, Q=16, H=64, prefix_lens=[185000], mask="chain",
+                            contiguous=True, q_scale=0.5),
+    "long185k_h8_contig": dict(seed=6, B=1, Q=16, H=8, prefix_lens=[185000], mask="chain",
+                               contiguous=True, q_scale=0.5),
 }
 
 CONFIG_ORDER = ["tiny", "p4k", "tree32k", "long185k", "batch8", "long185k_h8"]
