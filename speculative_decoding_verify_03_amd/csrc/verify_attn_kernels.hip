@@ -209,10 +209,10 @@ constexpr int kPBytes = 2 * 64 * 16;                    // one pair's P: two 16-
 constexpr int kRegKSteps = 16;                          // query k-steps held in VGPRs
 constexpr int kLdsKSteps = kHalfKSteps - kRegKSteps;    // the rest are re-read from LDS
 constexpr int kQParkBytes = kLdsKSteps * 64 * 16;       // per wave
-constexpr int kOffXchg = kRingS * kTileBytes;                      // 110592
-constexpr int kOffP = kOffXchg + kPairs * kXchgBytes;              // 126976
-constexpr int kOffAlpha = kOffP + 2 * kPairs * kPBytes;            // 143360: P, two tile parities
-constexpr int kOffFlag = kOffAlpha + 2 * kRowsPerWG * 4;           // 144384: rescale factors, two parities
+constexpr int kOffXchg = kRingS * kTileBytes;                      // 110592: partial-score hand-over
+constexpr int kOffP = kOffXchg + kPairs * kXchgBytes;              // 126976: P, two tile parities
+constexpr int kOffAlpha = kOffP + 2 * kPairs * kPBytes;            // 143360: rescale factors, two parities
+constexpr int kOffFlag = kOffAlpha + 2 * kRowsPerWG * 4;           // 144384: rescale flags, two parities
 constexpr int kOffSlots = kOffFlag + 64;                           // 144448: slot-index ring
 constexpr int kSlotRing = 8;                                       // 256 bytes per tile
 constexpr int kGatherAhead = 3;                                    // tile u+3 is gathered while tile u is applied
