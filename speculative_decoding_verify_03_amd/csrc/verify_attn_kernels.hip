@@ -399,7 +399,8 @@ split_kernel(SplitArgs a) {
   auto pbuf_of = [&](int v) { return pbuf + (v & 1) * (kPairs * kPBytes); };
   auto abuf_of = [&](int v) { return abuf + (v & 1) * (kRowsPerWG * 4); };
   auto fbuf_of = [&](int v) { return fbuf + (v & 1) * 16; };
-  // O^T *= alpha(v) for row blocks whose running max grew in tile v (rare).
+  // O^T *= alpha(v) when some row's running max grew in tile v (rare); rows
+  // whose max did not grow carry alpha = 1.
   auto rescale = [&](int v) {
     const i32x4 flags = *reinterpret_cast<LDS_AS const i32x4*>(fbuf_of(v));
     if (flags[0] | flags[1] | flags[2] | flags[3]) {
