@@ -88,7 +88,10 @@ __device__ __forceinline__ GatherLane gather_lane(int gw, int lane) {
 
 // Issue this wave's share of one tile gather (exactly kGatherLoads load
 // instructions). `slot` is the pool row of the lane's key (any out-of-range
-// value for an absent position: zero row).
+// value for an absent position: zero row). The loads carry the nontemporal
+// cache policy: a workgroup reads each row once, and with it one CU sustains
+// about twice the gather rate it reaches under the default policy.
+constexpr int kGatherPolicy = 2;   // cache-policy bit nt
 __device__ __forceinline__ void issue_tile_gather(const char* kv_pool, int64_t num_slots, int32_t slot,
                                                   LDS_AS char* tile, const GatherLane& gl) {
   const char* row = (slot >= 0 && slot < num_slots) ? kv_pool + (int64_t)slot * kRowBytes
@@ -96,7 +99,7 @@ __device__ __forceinline__ void issue_tile_gather(const char* kv_pool, int64_t n
   row += gl.coff;
 #pragma unroll
   for (int L = 0; L < kGatherLoads; ++L)
-    __builtin_amdgcn_global_load_lds(row + L * 128, tile + (gl.kg * 9 + L) * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(row + L * 128, tile + (gl.kg * 9 + L) * 1024, 16, 0, kGatherPolicy);
 }
 
 __device__ __forceinline__ LDS_AS char* lds_cast(char* p) { return (LDS_AS char*)(p); }
@@ -216,17 +219,14 @@ constexpr int kOffFlag = kOffAlpha + 2 * kRowsPerWG * 4;           // 144384: re
 constexpr int kOffSlots = kOffFlag + 64;                           // 144448: slot-index ring
 constexpr int kSlotRing = 8;                                       // 256 bytes per tile
 constexpr int kGatherAhead = 3;                                    // tile u+3 is gathered while tile u is applied
-constexpr int kSlotAhead = 7;                                      // slot copy distance, tiles
-constexpr int kPrefAhead = 5;                                      // L2 prefetch distance, tiles
-constexpr int kOffPref = kOffSlots + kSlotRing * 256;              // 146496: prefetch sink
-constexpr int kOffQPark = kOffPref + 256;                          // 146752
-constexpr int kSplitLds = kOffQPark + kSplitWaves * kQParkBytes;   // 163136
+constexpr int kSlotAhead = 5;                                      // slot copy distance, tiles
+constexpr int kOffQPark = kOffSlots + kSlotRing * 256;             // 146496
+constexpr int kSplitLds = kOffQPark + kSplitWaves * kQParkBytes;   // 162880
 static_assert(kSplitLds <= 160 * 1024, "split kernel LDS budget");
 // A slot copy issued in phase X of iteration v lands before the barrier that
-// ends phase X of iteration v+1; gathers read it kGatherAhead and prefetches
-// kPrefAhead tiles ahead of their tile.
-static_assert(kSlotAhead - 2 >= kGatherAhead && kSlotAhead - 2 >= kPrefAhead && kPrefAhead > kGatherAhead,
-              "slot copy distances");
+// ends phase X of iteration v+1; gathers read it kGatherAhead tiles ahead of
+// their tile.
+static_assert(kSlotAhead - 2 >= kGatherAhead, "slot copy distance");
 static_assert(kSlotRing > kSlotAhead && kGatherAhead == kRingS, "ring sizes");
 
 template <int V>
@@ -364,25 +364,6 @@ split_kernel(SplitArgs a) {
     return pos < kend ? a.kv_indices[sbase + pos] : -1;
   };
   auto issue = [&](int32_t slot, LDS_AS char* tile) { issue_tile_gather(a.kv_pool, a.num_slots, slot, tile, glane()); };
-  // L2 prefetch, one direct-to-LDS dword load per odd-half wave and tile
-  // (into a sink that nothing reads): lane m = 64(w-4) + l touches line
-  // rt + row_tiles * m of tile v's 288 lines (9 per key), so the row tiles of
-  // a chunk, which run side by side on one XCD, bring each line into L2 once
-  // between them, ahead of the gathers. Always exactly one instruction (lanes
-  // without a line read the zero row), which keeps the vmcnt counts exact.
-  auto prefetch = [&](int v, bool live) {
-    const int fl = fresh_lane();
-    const int m = (wave - 4) * 64 + fl;
-    const int li = rt + a.row_tiles * m;
-    const int key = li / 9;
-    const int line = li - key * 9;
-    const char* ptr = reinterpret_cast<const char*>(g_zero_row);
-    if (live && li < 9 * kUnit && kstart + (int64_t)v * kUnit + key < kend) {
-      const int32_t sl = *reinterpret_cast<LDS_AS const int32_t*>(slot_ring + (v % kSlotRing) * 256 + key * 4);
-      if (sl >= 0 && sl < a.num_slots) ptr = a.kv_pool + (int64_t)sl * kRowBytes + line * 128;
-    }
-    __builtin_amdgcn_global_load_lds(ptr, lds + kOffPref, 4, 0, 0);
-  };
 
   // Online-softmax state of the pair's rows (log2 domain; kept by the even
   // half) and this wave's output accumulators O^T: [row block][value block].
@@ -578,16 +559,16 @@ split_kernel(SplitArgs a) {
   //   phase X: the even wave applies tile u and computes its partial scores
   //            of tile u+1 (34 MFMAs) while the odd wave hands over its
   //            partial scores, issues the gather of tile u+3 into the freed
-  //            slot and the prefetches, and waits for tile u+2.
+  //            slot, and waits for tile u+2.
   // P, the rescale factors and flags are double-buffered by tile parity, as
   // the odd half reads those of tile u-1 while the even half writes tile u's.
   auto run = [&](auto pc) {
     constexpr int PP = decltype(pc)::value;
     if (nunits == 0) return;   // uniform across the workgroup
 
-    // Prologue: gathers of tiles 0-2, slot copies of tiles 3..kSlotAhead-1,
-    // and one prefetch that touches nothing, in the order that gives the loop
-    // its vmcnt counts; then wait for everything but tile 2.
+    // Prologue: gathers of tiles 0-2 and slot copies of tiles
+    // 3..kSlotAhead-1, in the order that gives the loop its vmcnt counts; then
+    // wait for everything but tile 2.
     if constexpr (PP == 1) {
       const int32_t s0 = load_slot(0);
       const int32_t s1 = load_slot(1);
@@ -596,8 +577,7 @@ split_kernel(SplitArgs a) {
       issue(s1, lds + kTileBytes);
       for (int v = kGatherAhead; v < kSlotAhead; ++v) load_slots_to_lds(v);
       issue(s2, lds + 2 * kTileBytes);
-      prefetch(0, false);
-      asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kGatherLoads) : "memory");
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     f32x16 sa = scores(lds);   // tile 0, both halves
@@ -649,14 +629,13 @@ split_kernel(SplitArgs a) {
         load_slots_to_lds(u + kSlotAhead);
         const int32_t slot = read_slot(u + kGatherAhead);
         issue(slot, tile);   // nobody reads tile u any more
-        prefetch(u + kPrefAhead, true);
         // Tile u+2 has landed once no more than the loads issued after it are
-        // outstanding: the prefetch of the previous phase X, this phase's slot
-        // copy (wave 4), nine gather loads and one prefetch. (The compiler
-        // does not track direct-to-LDS loads, so the wait is explicit; the
-        // barrier is issued by hand so that it does not drain tile u+3.)
-        if (wave == 4) asm volatile("s_waitcnt vmcnt(12)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(11)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // outstanding: this phase's slot copy (wave 4) and its nine gather
+        // loads. (The compiler does not track direct-to-LDS loads, so the wait
+        // is explicit; the barrier is issued by hand so that it does not drain
+        // tile u+3.)
+        if (wave == 4) asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(kGatherLoads + 1) : "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(kGatherLoads) : "memory");
       }
     }
     // the odd half's value update of the last tile
@@ -667,7 +646,7 @@ split_kernel(SplitArgs a) {
   };
   if (p == 0) run(IntC<0>{});
   else run(IntC<1>{});
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain prefetches before exit
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing gathers and slot copies before exit
 
   // ---- epilogue: the even halves publish 1/l per row (reusing the alpha
   // slots) and write lse; every wave normalises and writes its 64 dims.
