@@ -276,29 +276,44 @@ split_kernel(SplitArgs a) {
   const int r = rt * kRowsPerWG + pair * 32 + n;
   const bool row_ok = r < a.R;
   const int rr = row_ok ? r : 0;
+  // Tail-visibility bits of the lane's query (even half; all ones elsewhere).
+  // The first 16 positions are 16 unconditional byte loads (indices clamped
+  // into the row), so they cost one memory round trip, not one each.
   uint64_t tbits = ~0ull;
-  if (row_ok && p == 0) {
-    tbits = 0;
+  auto load_mask = [&]() {
     const uint8_t* mrow = a.tree_mask + ((int64_t)b * a.Q + rr / a.H) * a.Q;
-    for (int t = 0; t < a.Q; ++t) tbits |= (uint64_t)(mrow[t] != 0) << t;
-  }
+    uint64_t bits = 0;
+    for (int t0 = 0; t0 < a.Q; t0 += 16) {
+      uint32_t mb[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) mb[j] = mrow[t0 + j < a.Q ? t0 + j : a.Q - 1];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) bits |= (uint64_t)((t0 + j < a.Q) & (mb[j] != 0)) << (t0 + j);
+    }
+    tbits = row_ok ? bits : ~0ull;
+  };
 
   // Resident queries: for k-step ks of this wave's dim half, lane (n + 32h)
   // holds dims 288p + 16ks + 8h .. +7 of row n (zeros for padding rows). The
   // last kLdsKSteps k-steps are parked in LDS to stay within 256 VGPRs.
+  // Loading and placing are separate steps, so that a wave can have other
+  // loads in flight with the queries.
   bf16x8 qf[kRegKSteps];
   LDS_AS char* my_q = lds + kOffQPark + wave * kQParkBytes + lane * 16;
-  {
+  auto load_q = [&](u32x4 (&qv)[kHalfKSteps]) {
     const u32x4* qrow = reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * a.R + rr) * kLatent) +
                         p * (kHalfKSteps * 2) + h;
 #pragma unroll
+    for (int ks = 0; ks < kHalfKSteps; ++ks) qv[ks] = qrow[2 * ks];
+  };
+  auto place_q = [&](const u32x4 (&qv)[kHalfKSteps]) {
+#pragma unroll
     for (int ks = 0; ks < kHalfKSteps; ++ks) {
-      const u32x4 v = qrow[2 * ks];
-      const u32x4 vz = row_ok ? v : u32x4{0, 0, 0, 0};
+      const u32x4 vz = row_ok ? qv[ks] : u32x4{0, 0, 0, 0};
       if (ks < kRegKSteps) qf[ks] = __builtin_bit_cast(bf16x8, vz);
       else *reinterpret_cast<LDS_AS u32x4*>(my_q + (ks - kRegKSteps) * 1024) = vz;
     }
-  }
+  };
 
   // Lane-constant LDS offsets, recomputed where they are used (from
   // fresh_lane(), so they do not occupy registers across the loop).
@@ -566,18 +581,29 @@ split_kernel(SplitArgs a) {
     constexpr int PP = decltype(pc)::value;
     if (nunits == 0) return;   // uniform across the workgroup
 
-    // Prologue: gathers of tiles 0-2 and slot copies of tiles
-    // 3..kSlotAhead-1, in the order that gives the loop its vmcnt counts; then
-    // wait for everything but tile 2.
+    // Prologue. Odd half: pool rows of tiles 0-2 and the queries, loaded
+    // together (one memory round trip); then the gathers of tiles 0-2 and
+    // slot copies of tiles 3..kSlotAhead-1, in the order that gives the loop
+    // its vmcnt counts; then wait for everything but tile 2. (The queries are
+    // placed before the gathers go out: the compiler orders any use of a
+    // register load after every direct-to-LDS load issued behind it.) Even
+    // half: queries and mask row.
+    u32x4 qv[kHalfKSteps];
     if constexpr (PP == 1) {
       const int32_t s0 = load_slot(0);
       const int32_t s1 = load_slot(1);
       const int32_t s2 = load_slot(2);
+      load_q(qv);
+      place_q(qv);
       issue(s0, lds);
       issue(s1, lds + kTileBytes);
       for (int v = kGatherAhead; v < kSlotAhead; ++v) load_slots_to_lds(v);
       issue(s2, lds + 2 * kTileBytes);
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kGatherLoads) : "memory");
+    } else {
+      load_q(qv);
+      load_mask();
+      place_q(qv);
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     f32x16 sa = scores(lds);   // tile 0, both halves
