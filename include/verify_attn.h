@@ -118,7 +118,9 @@ int verify_attn_debug_gather(const void* kv_pool, const int32_t* kv_indices, int
 
 /*
  * The split plan verify_attn() would use for these sizes on the current
- * device: keys per chunk, the chunk capacity of the workspace, row tiles per
+ * device: the shortest keys per chunk (the device may pick a longer length,
+ * the shortest whose chunks fit in the chunk budget of the grid, from the
+ * actual prefix lengths), the chunk capacity of the workspace, row tiles per
  * sequence (128 query-head rows each) and the split-kernel grid size. Any
  * output pointer may be NULL. Returns VA_OK or VA_EINVAL.
  */

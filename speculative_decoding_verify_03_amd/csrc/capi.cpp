@@ -62,9 +62,10 @@ bool dims_ok(int B, int Q, int H, int64_t total_kv) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // The split plan. Workgroups are (chunk, 128-row tile) pairs and one
-// workgroup fills a compute unit (8 waves, ~159 KiB of LDS), so the batch is
-// cut into about floor(CUs / row_tiles) chunks of ~equal length; the plan
-// kernel then sizes each sequence's chunks from its own length.
+// workgroup fills a compute unit (8 waves, ~159 KiB of LDS), so the batch
+// gets a budget of floor(CUs / row_tiles) chunks; the plan kernel then picks
+// the shortest chunk length (at least total_kv / budget) whose chunks fit in
+// the budget.
 bool make_plan(int B, int Q, int H, int64_t total_kv, int ncu, va::Plan* p) {
   if (!dims_ok(B, Q, H, total_kv)) return false;
   const int64_t R = (int64_t)Q * H;
@@ -76,10 +77,11 @@ bool make_plan(int B, int Q, int H, int64_t total_kv, int ncu, va::Plan* p) {
   if (ov > 0) ideal = ov;
   if (ideal < va::kMinChunk && ov <= 0) ideal = va::kMinChunk;
   ideal = (ideal + va::kUnit - 1) / va::kUnit * va::kUnit;
-  p->target = (int32_t)target;
+  p->target = ov > 0 ? 0 : (int32_t)target;   // a forced length is used as is
   p->ideal_keys = (int32_t)ideal;
-  // Each sequence gets max(1, round(N_b / ideal)) chunks, so the batch never
-  // needs more than total_kv / ideal + B of them.
+  // The chunk length is at least ideal and a sequence of N_b keys takes
+  // ceil(N_b / length) chunks, so the batch never needs more than
+  // total_kv / ideal + B of them.
   const int64_t max_chunks = total_kv / ideal + B + 1;
   if (max_chunks > INT32_MAX / 8) return false;
   p->max_chunks = (int32_t)max_chunks;
@@ -169,7 +171,7 @@ int verify_attn(const void* q, const void* kv_pool, const int32_t* kv_indices,
     hipStream_t st = static_cast<hipStream_t>(stream);
 
     hipError_t e = va::launch_plan(prefix_lens, seq_off, chunk_off, chunk_len, B, Q, total_kv,
-                                   p.ideal_keys, p.max_chunks, st);
+                                   p.ideal_keys, p.target, p.max_chunks, st);
     if (e != hipSuccess) return fail(VA_EHIP, "plan launch: %s", hipGetErrorString(e));
 
     va::SplitArgs a;

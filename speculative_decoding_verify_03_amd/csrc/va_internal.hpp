@@ -16,10 +16,12 @@ constexpr int kRowBlocksPerWG = 4;     // score blocks per workgroup (one per wa
 constexpr int kRowsPerWG = kRowsPerBlock * kRowBlocksPerWG;  // 128 rows per row tile
 constexpr int kMinChunk = 256;         // smallest chunk worth a workgroup (keys)
 
-// Host-side split plan (the device refines chunk sizes per sequence).
+// Host-side split plan (the device picks the chunk length from the sequence
+// lengths: the shortest one, not below ideal_keys, that needs at most
+// `target` chunks).
 struct Plan {
   int32_t row_tiles;    // ceil(Q*H / 128)
-  int32_t target;       // chunks the device should aim for over the whole batch
+  int32_t target;       // chunk budget over the whole batch; 0 = use ideal_keys as is
   int32_t ideal_keys;   // keys per chunk that would hit `target` exactly (multiple of 32)
   int32_t max_chunks;   // capacity of the partial buffers (chunks)
   int32_t grid;         // split-kernel workgroups
@@ -50,7 +52,7 @@ struct SplitArgs {
 
 hipError_t launch_plan(const int32_t* prefix_lens, int64_t* seq_off, int32_t* chunk_off,
                        int32_t* chunk_len, int B, int Q, int64_t total_kv, int ideal_keys,
-                       int max_chunks, hipStream_t stream);
+                       int target, int max_chunks, hipStream_t stream);
 hipError_t launch_split(const SplitArgs& a, int grid, hipStream_t stream);
 hipError_t launch_merge(const float* part_o, const float* part_lse, const int32_t* chunk_off,
                         float* out, float* lse, int B, int R, hipStream_t stream);

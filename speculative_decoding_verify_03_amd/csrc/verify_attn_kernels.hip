@@ -133,16 +133,61 @@ __device__ __forceinline__ void bf16x4_to_f16(u32x2 v, f16x8& dst, int base) {
 }
 
 // ---------------------------------------------------------------------------
-// Plan: per-sequence KV offsets, balanced chunk lengths and chunk offsets.
+// Plan: per-sequence KV offsets, chunk offsets and one chunk length L for the
+// batch. Every chunk but a sequence's last holds exactly L keys, so L is the
+// critical path of the split kernel. With a chunk budget (target > 0) L is
+// the smallest multiple of 32 keys, not below ideal_keys, for which the batch
+// needs at most `target` chunks; without one (target == 0), or when the batch
+// has at least `target` sequences, L = ideal_keys.
 // ---------------------------------------------------------------------------
+// Sum over the 256 threads of the workgroup (every thread gets the total).
+__device__ __forceinline__ int64_t block_sum(int64_t v, int64_t* s_red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  __syncthreads();   // the previous call's readers are done
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return s_red[0] + s_red[1] + s_red[2] + s_red[3];
+}
+
 __global__ void __launch_bounds__(256) plan_kernel(const int32_t* __restrict__ prefix_lens,
                                                    int64_t* __restrict__ seq_off,
                                                    int32_t* __restrict__ chunk_off,
                                                    int32_t* __restrict__ chunk_len, int B, int Q,
-                                                   int64_t total_kv, int ideal_keys, int max_chunks) {
+                                                   int64_t total_kv, int ideal_keys, int target,
+                                                   int max_chunks) {
   __shared__ int64_t s_n[256];
   __shared__ int32_t s_c[256];
+  __shared__ int64_t s_red[4];
   const int tid = threadIdx.x;
+  auto keys_of = [&](int i) -> int64_t {   // N_b = clamped prefix + Q
+    int64_t p = prefix_lens[i];
+    p = p < 0 ? 0 : (p > total_kv ? total_kv : p);
+    return p + Q;
+  };
+
+  int64_t L = ideal_keys;
+  if (target > B) {
+    // Chunks needed at length `len`: sum over b of ceil(N_b / len). It is at
+    // most sum N_b / len + B, so lengths from sum N_b / (target - B) on fit.
+    int64_t part = 0;
+    for (int i = tid; i < B; i += 256) part += keys_of(i);
+    const int64_t nsum = block_sum(part, s_red);
+    auto count = [&](int64_t len) -> int64_t {
+      int64_t cnt = 0;
+      for (int i = tid; i < B; i += 256) cnt += (keys_of(i) + len - 1) / len;
+      return block_sum(cnt, s_red);
+    };
+    int64_t lo = ideal_keys / kUnit;
+    int64_t hi = (nsum / (target - B) + kUnit) / kUnit;
+    if (hi < lo) hi = lo;
+    while (lo < hi) {   // uniform across the workgroup
+      const int64_t mid = (lo + hi) >> 1;
+      if (count(mid * kUnit) <= target) hi = mid; else lo = mid + 1;
+    }
+    L = lo * kUnit;
+  }
+
   int64_t carry_n = 0;
   int32_t carry_c = 0;
   for (int base = 0; base < B; base += 256) {
@@ -150,16 +195,9 @@ __global__ void __launch_bounds__(256) plan_kernel(const int32_t* __restrict__ p
     int64_t nb = 0;
     int32_t cb = 0;
     if (i < B) {
-      int64_t p = prefix_lens[i];
-      p = p < 0 ? 0 : (p > total_kv ? total_kv : p);
-      nb = p + Q;
-      // round(N_b / ideal) chunks, at least one; then equal 32-key-aligned lengths
-      int64_t n = (nb + ideal_keys / 2) / ideal_keys;
-      if (n < 1) n = 1;
-      int64_t len = (nb + n - 1) / n;
-      len = (len + kUnit - 1) / kUnit * kUnit;
-      cb = (int32_t)((nb + len - 1) / len);
-      chunk_len[i] = (int32_t)len;
+      nb = keys_of(i);
+      cb = (int32_t)((nb + L - 1) / L);
+      chunk_len[i] = (int32_t)L;
     }
     s_n[tid] = nb;
     s_c[tid] = cb;
@@ -228,6 +266,11 @@ static_assert(kSplitLds <= 160 * 1024, "split kernel LDS budget");
 // their tile.
 static_assert(kSlotAhead - 2 >= kGatherAhead, "slot copy distance");
 static_assert(kSlotRing > kSlotAhead && kGatherAhead == kRingS, "ring sizes");
+// Epilogue staging: one 32-row block of a wave's 64 dims, rows padded to 272
+// bytes, per wave, inside the tile ring.
+constexpr int kStageRow = kWaveDvBlocks * 32 * 4 + 16;
+constexpr int kStageBytes = 32 * kStageRow;
+static_assert(kSplitWaves * kStageBytes <= kOffXchg, "epilogue staging fits in the tile ring");
 
 template <int V>
 struct IntC {
@@ -686,21 +729,30 @@ split_kernel(SplitArgs a) {
       if (row_ok && h == 0) a.part_lse[(int64_t)c * a.R + r] = lse_v;
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // The normalised block goes out through a wave-private LDS staging area
+    // (the tile ring is free now): written in the accumulator layout, read
+    // back row-major, so that every store instruction writes four rows of 256
+    // contiguous bytes (whole 128-byte lines) instead of 32-byte pieces of 32
+    // rows. Rows are padded to 272 bytes against bank conflicts.
+    LDS_AS char* stg = lds + wave * kStageBytes;
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb) {
-      const int rw = rt * kRowsPerWG + rb * 32 + n;
       const float inv = *reinterpret_cast<LDS_AS const float*>(abuf + (rb * 32 + n) * 4);
-      if (rw < a.R) {
-        float* orow = a.part_o + ((int64_t)c * a.R + rw) * kValue + wave * kWaveDvBlocks * 32;
 #pragma unroll
-        for (int db = 0; db < kWaveDvBlocks; ++db) {
+      for (int db = 0; db < kWaveDvBlocks; ++db)
 #pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            const f32x4 v = {o[rb][db][4 * qd] * inv, o[rb][db][4 * qd + 1] * inv,
-                             o[rb][db][4 * qd + 2] * inv, o[rb][db][4 * qd + 3] * inv};
-            *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * qd + 4 * h) = v;
-          }
-        }
+        for (int qd = 0; qd < 4; ++qd)
+          *reinterpret_cast<LDS_AS f32x4*>(stg + n * kStageRow + (db * 32 + 8 * qd + 4 * h) * 4) =
+              f32x4{o[rb][db][4 * qd] * inv, o[rb][db][4 * qd + 1] * inv, o[rb][db][4 * qd + 2] * inv,
+                    o[rb][db][4 * qd + 3] * inv};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int row = 4 * k + (lane >> 4);
+        const int ch = lane & 15;
+        const f32x4 v = *reinterpret_cast<LDS_AS const f32x4*>(stg + row * kStageRow + ch * 16);
+        const int rw = rt * kRowsPerWG + rb * 32 + row;
+        if (rw < a.R)
+          *reinterpret_cast<f32x4*>(a.part_o + ((int64_t)c * a.R + rw) * kValue + wave * kWaveDvBlocks * 32 + ch * 4) = v;
       }
     }
   }
@@ -823,9 +875,9 @@ __global__ void __launch_bounds__(kGatherWaves * 64) debug_gather_kernel(const c
 // ---------------------------------------------------------------------------
 hipError_t launch_plan(const int32_t* prefix_lens, int64_t* seq_off, int32_t* chunk_off,
                        int32_t* chunk_len, int B, int Q, int64_t total_kv, int ideal_keys,
-                       int max_chunks, hipStream_t stream) {
+                       int target, int max_chunks, hipStream_t stream) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, prefix_lens, seq_off, chunk_off,
-                     chunk_len, B, Q, total_kv, ideal_keys, max_chunks);
+                     chunk_len, B, Q, total_kv, ideal_keys, target, max_chunks);
   return hipGetLastError();
 }
 
