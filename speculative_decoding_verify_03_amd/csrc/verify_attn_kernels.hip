@@ -138,7 +138,7 @@ __device__ __forceinline__ void bf16x4_to_f16(u32x2 v, f16x8& dst, int base) {
 // critical path of the split kernel. With a chunk budget (target > 0) L is
 // the smallest multiple of 32 keys, not below ideal_keys, for which the batch
 // needs at most `target` chunks; without one (target == 0), or when the batch
-// has at least `target` sequences, L = ideal_keys.
+// has at least `target` (or more than 256) sequences, L = ideal_keys.
 // ---------------------------------------------------------------------------
 // Sum over the 256 threads of the workgroup (every thread gets the total).
 __device__ __forceinline__ int64_t block_sum(int64_t v, int64_t* s_red) {
@@ -167,23 +167,22 @@ __global__ void __launch_bounds__(256) plan_kernel(const int32_t* __restrict__ p
   };
 
   int64_t L = ideal_keys;
-  if (target > B) {
-    // Chunks needed at length `len`: sum over b of ceil(N_b / len). It is at
-    // most sum N_b / len + B, so lengths from sum N_b / (target - B) on fit.
-    int64_t part = 0;
-    for (int i = tid; i < B; i += 256) part += keys_of(i);
-    const int64_t nsum = block_sum(part, s_red);
-    auto count = [&](int64_t len) -> int64_t {
-      int64_t cnt = 0;
-      for (int i = tid; i < B; i += 256) cnt += (keys_of(i) + len - 1) / len;
-      return block_sum(cnt, s_red);
-    };
+  if (target > B && B <= 256) {
+    // Thread b holds N_b. Chunks needed at length
+    // `len`: sum over b of ceil(N_b / len), at most sum N_b / len + B, so
+    // lengths from sum N_b / (target - B) on fit.
+    const int64_t mine = tid < B ? keys_of(tid) : 0;
+    auto count = [&](int64_t len) -> int64_t { return block_sum((mine + len - 1) / len, s_red); };
     int64_t lo = ideal_keys / kUnit;
-    int64_t hi = (nsum / (target - B) + kUnit) / kUnit;
-    if (hi < lo) hi = lo;
-    while (lo < hi) {   // uniform across the workgroup
-      const int64_t mid = (lo + hi) >> 1;
-      if (count(mid * kUnit) <= target) hi = mid; else lo = mid + 1;
+    if (count(lo * kUnit) > target) {   // uniform across the workgroup
+      const int64_t nsum = block_sum(mine, s_red);
+      int64_t hi = (nsum / (target - B) + kUnit) / kUnit;
+      if (hi <= lo) hi = lo + 1;
+      ++lo;   // lo itself does not fit
+      while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (count(mid * kUnit) <= target) hi = mid; else lo = mid + 1;
+      }
     }
     L = lo * kUnit;
   }
