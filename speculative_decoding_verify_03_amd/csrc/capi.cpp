@@ -63,7 +63,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // The split plan. Workgroups are (chunk, 128-row tile) pairs and one
 // workgroup fills a compute unit (8 waves, ~159 KiB of LDS), so the batch
-// gets a budget of floor(CUs / row_tiles) chunks; the plan kernel then picks
+// gets a budget of floor(CUs / row_tiles) chunks; the split kernel then picks
 // the shortest chunk length (at least total_kv / budget) whose chunks fit in
 // the budget.
 bool make_plan(int B, int Q, int H, int64_t total_kv, int ncu, va::Plan* p) {
@@ -89,12 +89,8 @@ bool make_plan(int B, int Q, int H, int64_t total_kv, int ncu, va::Plan* p) {
   if (grid > INT32_MAX) return false;
   p->grid = (int32_t)grid;
   size_t off = 0;
-  p->off_seq = off;
-  off += sizeof(int64_t) * (size_t)(B + 1);
   p->off_chunk = off;
   off += sizeof(int32_t) * (size_t)(B + 1);
-  p->off_len = off;
-  off += sizeof(int32_t) * (size_t)B;
   off = align_up(off, 256);
   p->off_lse = off;
   off += sizeof(float) * (size_t)max_chunks * (size_t)R;
@@ -163,16 +159,11 @@ int verify_attn(const void* q, const void* kv_pool, const int32_t* kv_indices,
       return fail(VA_ENOSPC, "workspace of %zu bytes < %zu needed", workspace_bytes, p.bytes);
 
     char* ws = static_cast<char*>(workspace);
-    auto* seq_off = reinterpret_cast<int64_t*>(ws + p.off_seq);
     auto* chunk_off = reinterpret_cast<int32_t*>(ws + p.off_chunk);
-    auto* chunk_len = reinterpret_cast<int32_t*>(ws + p.off_len);
     auto* part_lse = reinterpret_cast<float*>(ws + p.off_lse);
     auto* part_o = reinterpret_cast<float*>(ws + p.off_o);
     hipStream_t st = static_cast<hipStream_t>(stream);
-
-    hipError_t e = va::launch_plan(prefix_lens, seq_off, chunk_off, chunk_len, B, Q, total_kv,
-                                   p.ideal_keys, p.target, p.max_chunks, st);
-    if (e != hipSuccess) return fail(VA_EHIP, "plan launch: %s", hipGetErrorString(e));
+    hipError_t e = hipSuccess;
 
     va::SplitArgs a;
     a.q = static_cast<const uint16_t*>(q);
@@ -180,9 +171,7 @@ int verify_attn(const void* q, const void* kv_pool, const int32_t* kv_indices,
     a.kv_indices = kv_indices;
     a.prefix_lens = prefix_lens;
     a.tree_mask = tree_mask;
-    a.seq_off = seq_off;
     a.chunk_off = chunk_off;
-    a.chunk_len = chunk_len;
     a.part_o = part_o;
     a.part_lse = part_lse;
     a.num_slots = num_slots;
@@ -192,6 +181,9 @@ int verify_attn(const void* q, const void* kv_pool, const int32_t* kv_indices,
     a.H = H;
     a.R = Q * H;
     a.row_tiles = p.row_tiles;
+    a.ideal_keys = p.ideal_keys;
+    a.target = p.target;
+    a.max_chunks = p.max_chunks;
     a.c_log2 = scale * 1.4426950408889634f;
     const bool timed = g_split_start != nullptr && g_split_stop != nullptr;
     if (timed && (e = hipEventRecord(g_split_start, st)) != hipSuccess)

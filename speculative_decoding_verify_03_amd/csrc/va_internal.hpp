@@ -16,18 +16,17 @@ constexpr int kRowBlocksPerWG = 4;     // score blocks per workgroup (one per wa
 constexpr int kRowsPerWG = kRowsPerBlock * kRowBlocksPerWG;  // 128 rows per row tile
 constexpr int kMinChunk = 256;         // smallest chunk worth a workgroup (keys)
 
-// Host-side split plan (the device picks the chunk length from the sequence
-// lengths: the shortest one, not below ideal_keys, that needs at most
-// `target` chunks).
+// Host-side split plan (the split kernel picks the chunk length from the
+// sequence lengths: the shortest one, not below ideal_keys, that needs at
+// most `target` chunks).
 struct Plan {
   int32_t row_tiles;    // ceil(Q*H / 128)
   int32_t target;       // chunk budget over the whole batch; 0 = use ideal_keys as is
   int32_t ideal_keys;   // keys per chunk that would hit `target` exactly (multiple of 32)
   int32_t max_chunks;   // capacity of the partial buffers (chunks)
   int32_t grid;         // split-kernel workgroups
-  size_t off_seq;       // workspace byte offsets
-  size_t off_chunk;
-  size_t off_len;
+  size_t off_chunk;     // workspace byte offsets
+
   size_t off_lse;
   size_t off_o;
   size_t bytes;         // total workspace bytes
@@ -39,20 +38,16 @@ struct SplitArgs {
   const int32_t* kv_indices;
   const int32_t* prefix_lens;
   const uint8_t* tree_mask;
-  const int64_t* seq_off;
-  const int32_t* chunk_off;
-  const int32_t* chunk_len;
+  int32_t* chunk_off;      // written by workgroup 0: [B + 1] chunk offsets for the merge
   float* part_o;
   float* part_lse;
   int64_t num_slots;
   int64_t total_kv;
   int32_t B, Q, H, R, row_tiles;
+  int32_t ideal_keys, target, max_chunks;   // chunk plan inputs (see Plan)
   float c_log2;  // scale * log2(e)
 };
 
-hipError_t launch_plan(const int32_t* prefix_lens, int64_t* seq_off, int32_t* chunk_off,
-                       int32_t* chunk_len, int B, int Q, int64_t total_kv, int ideal_keys,
-                       int target, int max_chunks, hipStream_t stream);
 hipError_t launch_split(const SplitArgs& a, int grid, hipStream_t stream);
 hipError_t launch_merge(const float* part_o, const float* part_lse, const int32_t* chunk_off,
                         float* out, float* lse, int B, int R, hipStream_t stream);

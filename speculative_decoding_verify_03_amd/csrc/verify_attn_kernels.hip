@@ -133,95 +133,139 @@ __device__ __forceinline__ void bf16x4_to_f16(u32x2 v, f16x8& dst, int base) {
 }
 
 // ---------------------------------------------------------------------------
-// Plan: per-sequence KV offsets, chunk offsets and one chunk length L for the
-// batch. Every chunk but a sequence's last holds exactly L keys, so L is the
-// critical path of the split kernel. With a chunk budget (target > 0) L is
-// the smallest multiple of 32 keys, not below ideal_keys, for which the batch
-// needs at most `target` chunks; without one (target == 0), or when the batch
-// has at least `target` (or more than 256) sequences, L = ideal_keys.
+// Chunk plan, computed by every split workgroup at its start (identically, from
+// prefix_lens alone): one chunk length L for the batch, and where chunk c sits.
+// Every chunk but a sequence's last holds exactly L keys, so L is the split
+// kernel's critical path. With a chunk budget (target > 0) L is the smallest
+// multiple of 32 keys, not below ideal_keys, for which the batch needs at
+// most `target` chunks; without one (target == 0), or when the batch has at
+// least `target` (or more than 512) sequences, L = ideal_keys. Sequence b owns
+// chunks [chunk_off[b], chunk_off[b+1]) with chunk_off the running sum of
+// ceil(N_b / L), N_b = clamped prefix + Q; its positions start at the running
+// sum of N.
 // ---------------------------------------------------------------------------
-// Sum over the 256 threads of the workgroup (every thread gets the total).
-__device__ __forceinline__ int64_t block_sum(int64_t v, int64_t* s_red) {
+constexpr int kPlanThreads = 512;   // the split kernel's workgroup size
+
+struct ChunkPlan {
+  int64_t L;       // keys per chunk
+  int64_t sbase;   // first position of the chunk's sequence
+  int64_t P;       // its clamped prefix length
+  int32_t b;       // its sequence
+  int32_t coff;    // its first chunk
+  int32_t total;   // chunks of the batch (capped at max_chunks)
+};
+
+// Sum over the kPlanThreads threads of the workgroup; every thread gets the total.
+// `red` holds 8 int64 in LDS.
+__device__ __forceinline__ int64_t block_sum(int64_t v, LDS_AS int64_t* red) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  __syncthreads();   // the previous call's readers are done
-  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = v;
+  __syncthreads();   // readers of the previous sum are done
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  return s_red[0] + s_red[1] + s_red[2] + s_red[3];
+  int64_t t = 0;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) t += red[w];
+  return t;
 }
 
-__global__ void __launch_bounds__(256) plan_kernel(const int32_t* __restrict__ prefix_lens,
-                                                   int64_t* __restrict__ seq_off,
-                                                   int32_t* __restrict__ chunk_off,
-                                                   int32_t* __restrict__ chunk_len, int B, int Q,
-                                                   int64_t total_kv, int ideal_keys, int target,
-                                                   int max_chunks) {
-  __shared__ int64_t s_n[256];
-  __shared__ int32_t s_c[256];
-  __shared__ int64_t s_red[4];
-  const int tid = threadIdx.x;
-  auto keys_of = [&](int i) -> int64_t {   // N_b = clamped prefix + Q
-    int64_t p = prefix_lens[i];
-    p = p < 0 ? 0 : (p > total_kv ? total_kv : p);
-    return p + Q;
-  };
+// Inclusive prefix sum over the 64 lanes of a wave.
+template <typename T>
+__device__ __forceinline__ T wave_scan(T v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const T u = __shfl_up(v, off);
+    if (lane >= off) v += u;
+  }
+  return v;
+}
 
-  int64_t L = ideal_keys;
-  if (target > B && B <= 256) {
-    // Thread b holds N_b. Chunks needed at length
-    // `len`: sum over b of ceil(N_b / len), at most sum N_b / len + B, so
-    // lengths from sum N_b / (target - B) on fit.
+// All kPlanThreads threads call this with the same c. `scratch` is 256 bytes of LDS
+// that nothing else uses until the workgroup's next barrier after the call.
+// The workgroup that gets write_offsets stores chunk_off[0..B] for the merge.
+__device__ ChunkPlan chunk_plan(const SplitArgs& a, int c, bool write_offsets, LDS_AS char* scratch) {
+  LDS_AS int64_t* red = reinterpret_cast<LDS_AS int64_t*>(scratch);        // 8 sums
+  LDS_AS int64_t* wn = red + 8;                                            // 8 wave totals of N
+  LDS_AS int32_t* wc = reinterpret_cast<LDS_AS int32_t*>(red + 16);        // 8 wave totals of chunks
+  LDS_AS int64_t* own = red + 20;                                          // b, coff, sbase, P of chunk c
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int B = a.B;
+  auto keys_of = [&](int i) -> int64_t {
+    int64_t pl = a.prefix_lens[i];
+    pl = pl < 0 ? 0 : (pl > a.total_kv ? a.total_kv : pl);
+    return pl + a.Q;
+  };
+  if (tid == 0) own[0] = -1;
+
+  int64_t L = a.ideal_keys;
+  if (a.target > B && B <= kPlanThreads) {
+    // Thread b holds N_b. Chunks needed at length `len`: the sum of
+    // ceil(N_b / len), at most sum N_b / len + B, so lengths from
+    // sum N_b / (target - B) on fit.
     const int64_t mine = tid < B ? keys_of(tid) : 0;
-    auto count = [&](int64_t len) -> int64_t { return block_sum((mine + len - 1) / len, s_red); };
-    int64_t lo = ideal_keys / kUnit;
-    if (count(lo * kUnit) > target) {   // uniform across the workgroup
-      const int64_t nsum = block_sum(mine, s_red);
-      int64_t hi = (nsum / (target - B) + kUnit) / kUnit;
+    auto count = [&](int64_t len) -> int64_t { return block_sum((mine + len - 1) / len, red); };
+    int64_t lo = a.ideal_keys / kUnit;
+    if (count(lo * kUnit) > a.target) {   // uniform across the workgroup
+      const int64_t nsum = block_sum(mine, red);
+      int64_t hi = (nsum / (a.target - B) + kUnit) / kUnit;
       if (hi <= lo) hi = lo + 1;
       ++lo;   // lo itself does not fit
       while (lo < hi) {
         const int64_t mid = (lo + hi) >> 1;
-        if (count(mid * kUnit) <= target) hi = mid; else lo = mid + 1;
+        if (count(mid * kUnit) <= a.target) hi = mid; else lo = mid + 1;
       }
     }
     L = lo * kUnit;
   }
 
+  // Running sums over the batch, kPlanThreads sequences per pass.
   int64_t carry_n = 0;
   int32_t carry_c = 0;
-  for (int base = 0; base < B; base += 256) {
+  for (int base = 0; base < B; base += kPlanThreads) {
     const int i = base + tid;
-    int64_t nb = 0;
-    int32_t cb = 0;
-    if (i < B) {
-      nb = keys_of(i);
-      cb = (int32_t)((nb + L - 1) / L);
-      chunk_len[i] = (int32_t)L;
+    const int64_t nb = i < B ? keys_of(i) : 0;
+    const int32_t cb = i < B ? (int32_t)((nb + L - 1) / L) : 0;
+    int64_t in_n = wave_scan(nb, lane);
+    int32_t in_c = wave_scan(cb, lane);
+    __syncthreads();   // readers of the previous pass's totals are done
+    if (lane == 63) {
+      wn[wave] = in_n;
+      wc[wave] = in_c;
     }
-    s_n[tid] = nb;
-    s_c[tid] = cb;
     __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const int64_t an = tid >= off ? s_n[tid - off] : 0;
-      const int32_t ac = tid >= off ? s_c[tid - off] : 0;
-      __syncthreads();
-      s_n[tid] += an;
-      s_c[tid] += ac;
-      __syncthreads();
+    int64_t tot_n = 0;
+    int32_t tot_c = 0;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      if (w < wave) {
+        in_n += wn[w];
+        in_c += wc[w];
+      }
+      tot_n += wn[w];
+      tot_c += wc[w];
     }
-    if (i < B) {
-      seq_off[i] = carry_n + s_n[tid] - nb;
-      const int32_t co = carry_c + s_c[tid] - cb;
-      chunk_off[i] = co < max_chunks ? co : max_chunks;
+    const int32_t ex_c = carry_c + in_c - cb;
+    const int64_t ex_n = carry_n + in_n - nb;
+    if (i < B && ex_c <= c && c < ex_c + cb) {
+      own[0] = i;
+      own[1] = ex_c;
+      own[2] = ex_n;
+      own[3] = nb - a.Q;
     }
-    carry_n += s_n[255];
-    carry_c += s_c[255];
-    __syncthreads();
+    if (write_offsets && i < B) a.chunk_off[i] = ex_c < a.max_chunks ? ex_c : a.max_chunks;
+    carry_n += tot_n;
+    carry_c += tot_c;
   }
-  if (tid == 0) {
-    seq_off[B] = carry_n;
-    chunk_off[B] = carry_c < max_chunks ? carry_c : max_chunks;
-  }
+  if (write_offsets && tid == 0) a.chunk_off[B] = carry_c < a.max_chunks ? carry_c : a.max_chunks;
+  __syncthreads();
+  ChunkPlan cp;
+  cp.L = L;
+  cp.total = carry_c < a.max_chunks ? carry_c : a.max_chunks;
+  cp.b = (int32_t)own[0];
+  cp.coff = (int32_t)own[1];
+  cp.sbase = own[2];
+  cp.P = own[3];
+  return cp;
 }
 
 // ---------------------------------------------------------------------------
@@ -239,6 +283,7 @@ __global__ void __launch_bounds__(256) plan_kernel(const int32_t* __restrict__ p
 // ---------------------------------------------------------------------------
 constexpr int kSplitWaves = 8;
 constexpr int kSplitThreads = kSplitWaves * 64;
+static_assert(kSplitThreads == kPlanThreads, "the chunk plan runs on the split workgroup");
 constexpr int kRingS = 3;                               // tiles resident in LDS
 constexpr int kPairs = 4;
 constexpr int kHalfKSteps = kKSteps / 2;                // 18 k-steps per wave
@@ -296,20 +341,16 @@ split_kernel(SplitArgs a) {
   const int y = wg >> 3;
   const int rt = y % a.row_tiles;
   const int c = (y / a.row_tiles) * 8 + xcd;
-  if (c >= a.chunk_off[a.B]) return;
-  int lo = 0, hi = a.B;  // chunk_off[lo] <= c < chunk_off[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.chunk_off[mid] <= c) lo = mid; else hi = mid;
-  }
-  const int b = lo;
-  int64_t P = a.prefix_lens[b];
-  P = P < 0 ? 0 : (P > a.total_kv ? a.total_kv : P);
+  // (P region of LDS as scratch: first written by the softmax of tile 0,
+  // after several barriers.)
+  const ChunkPlan cp = chunk_plan(a, c, wg == 0, lds + kOffP);
+  if (c >= cp.total) return;   // uniform across the workgroup
+  const int b = cp.b;
+  const int64_t P = cp.P;
   const int64_t N = P + a.Q;
-  const int64_t sbase = a.seq_off[b];
-  const int64_t clen = a.chunk_len[b];
-  const int64_t kstart = (int64_t)(c - a.chunk_off[b]) * clen;
-  int64_t kend = kstart + clen;
+  const int64_t sbase = cp.sbase;
+  const int64_t kstart = (int64_t)(c - cp.coff) * cp.L;
+  int64_t kend = kstart + cp.L;
   if (kend > N) kend = N;
   if (kend > a.total_kv - sbase) kend = a.total_kv - sbase;  // positions past the array are absent
   const int nunits = kend > kstart ? (int)((kend - kstart + kUnit - 1) / kUnit) : 0;
@@ -872,14 +913,6 @@ __global__ void __launch_bounds__(kGatherWaves * 64) debug_gather_kernel(const c
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_plan(const int32_t* prefix_lens, int64_t* seq_off, int32_t* chunk_off,
-                       int32_t* chunk_len, int B, int Q, int64_t total_kv, int ideal_keys,
-                       int target, int max_chunks, hipStream_t stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, stream, prefix_lens, seq_off, chunk_off,
-                     chunk_len, B, Q, total_kv, ideal_keys, target, max_chunks);
-  return hipGetLastError();
-}
-
 hipError_t launch_split(const SplitArgs& a, int grid, hipStream_t stream) {
   hipLaunchKernelGGL(split_kernel, dim3(grid), dim3(kSplitThreads), 0, stream, a);
   return hipGetLastError();
