@@ -122,13 +122,26 @@ def cpu_baseline(w, heads, min_seconds=10.0, max_reps=20):
     }
 
 
+class Evictor:
+    """Evicts the caches (L2 and the last-level cache) before a cold call by
+    reading a 1 GiB buffer: a reduction whose 4-byte result is dropped. A read
+    leaves no dirty lines behind; a 1 GiB fill would leave the last-level cache
+    full of dirty lines, whose write-back then competes with the timed call."""
+
+    def __init__(self, torch, dev):
+        self.buf = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        self.buf.sum()
+
+
 def _event_times(torch, fn, steps, flush=None):
     """Mean and median µs of `fn` over `steps` calls timed with HIP events on the
-    current stream (each preceded by a cache-evicting fill when `flush` is given)."""
+    current stream (each preceded by a cache eviction when `flush` is given)."""
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for e0, e1 in ev:
         if flush is not None:
-            flush.zero_()
+            flush()
         e0.record()
         fn()
         e1.record()
@@ -149,7 +162,7 @@ def bench_defrag(args, torch, va) -> int:
     n = int(w.total_kv)
     dst = torch.empty((n, 576), dtype=torch.int16, device=dev)
     new_idx = torch.empty(n, dtype=torch.int32, device=dev)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush = Evictor(torch, dev)
 
     def call():
         va.kv_defrag(src, idx, dst, 0, new_indices=new_idx)
@@ -249,7 +262,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="long185k", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-flush", action="store_true", help="skip the cache-evicting fill between calls")
+    ap.add_argument("--no-flush", action="store_true", help="skip the cache eviction between calls")
     ap.add_argument("--chunk", type=int, default=0, help="keys-per-chunk override (0 = automatic)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--op", default="attn", choices=["attn", "defrag", "tree_accept"],
@@ -291,7 +304,7 @@ def main() -> int:
     ws = va.alloc_workspace(w.B, w.Q, w.H, w.total_kv, device=dev)
     out = torch.empty((w.B, w.Q, w.H, 512), dtype=torch.float32, device=dev)
     lse = torch.empty((w.B, w.Q, w.H), dtype=torch.float32, device=dev)
-    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush = None if args.no_flush else Evictor(torch, dev)
     scale = float(w.scale)
 
     def call():
@@ -302,30 +315,38 @@ def main() -> int:
         call()
     torch.cuda.synchronize()
 
-    def timed(n, do_flush):
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
-        for e in ev:          # torch creates the HIP events on first record; the split
-            e[2].record()     # pair is then re-recorded by the library around the kernel
-            e[3].record()
-        torch.cuda.synchronize()
+    def timed(n, do_flush, split_events):
+        """Per-call times (us) of n calls; with split_events, of the split kernel
+        alone (the library records the pair around that launch) instead of the
+        whole call. The two are separate passes, so that the call times carry no
+        event records inside the call."""
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+        if split_events:
+            for e in ev:          # torch creates the HIP events on first record; the
+                e[0].record()     # pair is then re-recorded by the library
+                e[1].record()
+            torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(n):
             if do_flush:
-                flush.zero_()
-            va.set_split_events(ev[k][2], ev[k][3])
-            ev[k][0].record()
-            call()
-            ev[k][1].record()
+                flush()
+            if split_events:
+                va.set_split_events(ev[k][0], ev[k][1])
+                call()
+            else:
+                ev[k][0].record()
+                call()
+                ev[k][1].record()
         va.set_split_events(None, None)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        calls = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3   # us
-        splits = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e3
-        return calls, splits, wall
+        return np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3, wall
 
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    calls, splits, wall = timed(args.steps, flush is not None)
-    warm_calls, warm_splits, _ = timed(args.steps, False)
+    calls, wall = timed(args.steps, flush is not None, False)
+    splits, _ = timed(args.steps, flush is not None, True)
+    warm_calls, _ = timed(args.steps, False, False)
+    warm_splits, _ = timed(args.steps, False, True)
 
     us = float(calls.mean())
     abytes = algorithmic_bytes(w)
