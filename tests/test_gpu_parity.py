@@ -229,6 +229,49 @@ def test_random_shape_sweep(env, case):
         va.set_chunk_override(0)
 
 
+def _plan_model(w, plan, ncu):
+    """The chunk plan's rule written out plainly: one chunk length L for the batch,
+    the smallest multiple of 32 not below the host's shortest length for which the
+    batch needs at most CUs / row_tiles chunks (sought only when there are fewer
+    sequences than that budget, and at most 512), by brute force here; chunk
+    offsets are the running sum of ceil(N_b / L), N_b = clamped prefix + Q,
+    capped at the partial buffers' capacity."""
+    n = np.clip(w.prefix_lens.astype(np.int64), 0, w.total_kv) + w.Q
+    budget = max(1, ncu // plan["row_tiles"])
+    count = lambda length: int(np.sum(-(-n // length)))  # noqa: E731
+    length = plan["chunk_keys"]
+    if budget > w.B and w.B <= 512:
+        while count(length) > budget:
+            length += 32
+    off = np.concatenate([[0], np.cumsum(-(-n // length))])
+    return np.minimum(off, plan["max_chunks"]).astype(np.int32), length
+
+
+@pytest.mark.parametrize("label,B,Q,H,prefix", [
+    ("batch600_two_scan_passes", 600, 2, 4, (0, 60)),    # more sequences than the budget; two scan passes
+    ("batch300_over_budget", 300, 3, 4, (0, 80)),         # more sequences than the budget; one pass
+    ("batch100_length_search", 100, 4, 2, (696, 696)),    # the shortest length needs 300 chunks: searched
+    ("batch8_ragged_search", 8, 4, 2, (4000, 30000)),     # ragged lengths, searched
+])
+def test_chunk_plan_batches(env, label, B, Q, H, prefix):
+    """Large and ragged batches through the chunk plan that every split workgroup
+    computes for itself: parity with the oracle, and the chunk offsets that
+    workgroup 0 leaves at the start of the workspace for the merge (int32 [B+1])
+    equal the rule's."""
+    torch, va = env
+    w = make_workload(label, [916, B], B=B, Q=Q, H=H, prefix_range=prefix, mask="tree")
+    print(f"[parity] start {label}: B={B} Q={Q} H={H} total_kv={w.total_kv}", flush=True)
+    plan = va.query_plan(B, Q, H, w.total_kv)
+    ws = va.alloc_workspace(B, Q, H, w.total_kv)
+    ws.fill_(0xFF)
+    _check(env, w, label=label, workspace=ws)
+    got = ws[: 4 * (B + 1)].cpu().numpy().view(np.int32)
+    want, length = _plan_model(w, plan, torch.cuda.get_device_properties(0).multi_processor_count)
+    print(f"[parity] {label}: chunk length {length} (shortest allowed {plan['chunk_keys']}), "
+          f"{want[-1]} chunks", flush=True)
+    assert np.array_equal(got, want), f"{label}: chunk offsets differ from the plan rule"
+
+
 def test_defragmented_cache_full_size_bitwise_equal(env):
     """The 8-head 185k workload over a shuffled pool and over the same rows laid out
     contiguously (what KV defragmentation produces): same q, same rows, only the
