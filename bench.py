@@ -259,7 +259,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="long185k", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache eviction between calls")
@@ -315,38 +315,41 @@ def main() -> int:
         call()
     torch.cuda.synchronize()
 
-    def timed(n, do_flush, split_events):
-        """Per-call times (us) of n calls; with split_events, of the split kernel
-        alone (the library records the pair around that launch) instead of the
-        whole call. The two are separate passes, so that the call times carry no
-        event records inside the call."""
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
-        if split_events:
-            for e in ev:          # torch creates the HIP events on first record; the
-                e[0].record()     # pair is then re-recorded by the library
-                e[1].record()
-            torch.cuda.synchronize()
+    def timed(n, do_flush):
+        """n timed steps. Each step makes four calls, so that any drift of the
+        GPU's clocks during the run affects every figure alike: a cold call (after
+        a cache eviction when do_flush), a cold call timing the split kernel alone,
+        then a warm call and a warm split-kernel timing (each right after the
+        previous call). Whole calls are timed from the library's event before its
+        first launch (the split kernel) to an event after the call; split-kernel
+        timings use the library's event pair around that launch. Returns the four
+        arrays (us) and the wall time of the loop."""
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(n)]
+        for e in ev:          # torch creates the HIP events on first record; the
+            for x in e:       # library then re-records them inside the calls
+                x.record()
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(n):
-            if do_flush:
-                flush()
-            if split_events:
-                va.set_split_events(ev[k][0], ev[k][1])
+            e = ev[k]
+            for j, cold in ((0, True), (4, False)):
+                if cold and do_flush:
+                    flush()
+                va.set_split_events(e[j], None)
                 call()
-            else:
-                ev[k][0].record()
+                e[j + 1].record()
+                if cold and do_flush:
+                    flush()
+                va.set_split_events(e[j + 2], e[j + 3])
                 call()
-                ev[k][1].record()
-        va.set_split_events(None, None)
+            va.set_split_events(None, None)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        return np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e3, wall
+        t = lambda i: np.array([x[i].elapsed_time(x[i + 1]) for x in ev]) * 1e3  # noqa: E731
+        return t(0), t(2), t(4), t(6), wall
 
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    calls, wall = timed(args.steps, flush is not None, False)
-    splits, _ = timed(args.steps, flush is not None, True)
-    warm_calls, _ = timed(args.steps, False, False)
-    warm_splits, _ = timed(args.steps, False, True)
+    calls, splits, warm_calls, warm_splits, wall = timed(args.steps, flush is not None)
 
     us = float(calls.mean())
     abytes = algorithmic_bytes(w)
@@ -386,7 +389,7 @@ def main() -> int:
         "us_per_call_warm": round(float(warm_calls.mean()), 2),
         "split_kernel_us": round(split_us, 2),
         "split_kernel_us_warm": round(float(warm_splits.mean()), 2),
-        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+        "wall_ms_per_step_of_4_calls": round(wall / args.steps * 1e3, 4),
         "roofline": dict(roof, traffic=measured_traffic(args.config), kernel="split_kernel"),
     }
     if not args.no_cpu_baseline:

@@ -128,11 +128,13 @@ int verify_attn_query_plan(int B, int Q, int H, int64_t total_kv, int32_t* chunk
                            int32_t* max_chunks, int32_t* row_tiles, int32_t* grid);
 
 /*
- * Profiling hook (thread-local): when both are non-NULL, every later
- * verify_attn() call on this thread records start_event on its stream right
- * before launching the split kernel and stop_event right after it, so the
- * caller can time that kernel alone (events are hipEvent_t passed as void*,
- * created and owned by the caller). Passing NULL, NULL turns it off.
+ * Profiling hook (thread-local): every later verify_attn() call on this
+ * thread records start_event (if non-NULL) on its stream right before
+ * launching the split kernel, its first launch, and stop_event (if non-NULL)
+ * right after it. Both time the split kernel alone; start_event alone, with
+ * an event the caller records after the call, times the whole call from its
+ * first kernel. Events are hipEvent_t passed as void*, created and owned by
+ * the caller. Passing NULL, NULL turns it off.
  */
 void verify_attn_set_split_events(void* start_event, void* stop_event);
 

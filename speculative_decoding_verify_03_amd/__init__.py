@@ -114,7 +114,8 @@ def set_chunk_override(chunk_keys: int) -> None:
 
 
 def set_split_events(start_event=None, stop_event=None) -> None:
-    """Record these torch.cuda.Events around the split kernel of later calls (None: off)."""
+    """Record these torch.cuda.Events right before / after the split kernel of later
+    calls (either may be None: not recorded)."""
     h = lambda e: None if e is None else int(e.cuda_event)  # noqa: E731
     load_library().verify_attn_set_split_events(h(start_event), h(stop_event))
 

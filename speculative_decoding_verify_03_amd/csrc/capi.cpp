@@ -185,12 +185,11 @@ int verify_attn(const void* q, const void* kv_pool, const int32_t* kv_indices,
     a.target = p.target;
     a.max_chunks = p.max_chunks;
     a.c_log2 = scale * 1.4426950408889634f;
-    const bool timed = g_split_start != nullptr && g_split_stop != nullptr;
-    if (timed && (e = hipEventRecord(g_split_start, st)) != hipSuccess)
+    if (g_split_start != nullptr && (e = hipEventRecord(g_split_start, st)) != hipSuccess)
       return fail(VA_EHIP, "event record: %s", hipGetErrorString(e));
     e = va::launch_split(a, p.grid, st);
     if (e != hipSuccess) return fail(VA_EHIP, "split launch: %s", hipGetErrorString(e));
-    if (timed && (e = hipEventRecord(g_split_stop, st)) != hipSuccess)
+    if (g_split_stop != nullptr && (e = hipEventRecord(g_split_stop, st)) != hipSuccess)
       return fail(VA_EHIP, "event record: %s", hipGetErrorString(e));
 
     e = va::launch_merge(part_o, part_lse, chunk_off, out, lse, B, Q * H, st);
