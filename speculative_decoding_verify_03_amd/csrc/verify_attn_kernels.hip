@@ -803,17 +803,21 @@ split_kernel(SplitArgs a) {
 // One 256-thread workgroup per (row, quarter of the 512 value dims): thread
 // t handles 4 dims (t % 32) of the quarter for chunks c0 + (t / 32) + 8k, so
 // each wave reads two whole 512-byte row segments per step and the chunks
-// of a row are spread over 8 lanes; an LDS reduction combines them.
+// of a row are spread over 8 lanes. Each lane folds its chunks in one pass
+// with a running maximum (the log2 domain; earlier terms are rescaled when it
+// grows), loading the next four chunks while it folds the current four; an
+// LDS step then combines the 8 lanes.
 // ---------------------------------------------------------------------------
 constexpr int kMergeLanes = 8;   // chunk lanes per workgroup
+constexpr int kMergeBatch = 4;   // chunks per lane and load batch
 
 __global__ void __launch_bounds__(256) merge_kernel(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_lse,
                                                     const int32_t* __restrict__ chunk_off,
                                                     float* __restrict__ out, float* __restrict__ lse,
                                                     int B, int R) {
-  __shared__ float s_max[256];
   __shared__ f32x4 s_acc[kMergeLanes][32];
+  __shared__ float s_m[kMergeLanes];
   __shared__ float s_w[kMergeLanes];
   const int64_t grow = (int64_t)(blockIdx.x >> 2);
   const int qd = blockIdx.x & 3;
@@ -823,64 +827,82 @@ __global__ void __launch_bounds__(256) merge_kernel(const float* __restrict__ pa
   const int t = threadIdx.x;
   const int dl = t & 31, cl = t >> 5;
   const int c0 = chunk_off[b], c1 = chunk_off[b + 1];
-
-  // max of the partial lse over the row's chunks
-  float mx = -INFINITY;
-  for (int c = c0 + t; c < c1; c += 256) mx = fmaxf(mx, part_lse[(int64_t)c * R + r]);
-  s_max[t] = mx;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (t < off) s_max[t] = fmaxf(s_max[t], s_max[t + off]);
-    __syncthreads();
-  }
-  mx = s_max[0];
-
   float* orow = out + grow * kValue + qd * 128 + 4 * dl;
-  if (!(mx > -INFINITY)) {   // nothing visible in any chunk
+  if (c1 <= c0) {   // no chunk (only when the partial buffers ran out)
     if (cl == 0) *reinterpret_cast<f32x4*>(orow) = f32x4{0.f, 0.f, 0.f, 0.f};
     if (t == 0 && qd == 0) lse[grow] = -INFINITY;
     return;
   }
-  // weighted sums over this lane's chunks (weights exp(lse_s - max); empty
-  // chunks have lse_s = -inf and weight 0)
+
+  // Running maximum m (log2 units), weight sum and weighted sum of this
+  // lane's chunks. Chunks that are empty for the row (lse_s = -inf) weigh 0.
+  float m = -INFINITY, ws = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
   const float* obase = part_o + (int64_t)r * kValue + qd * 128 + 4 * dl;
+  // Batch of chunks cs + 8k; positions past the row's last chunk load that
+  // chunk again and count as empty.
+  auto load = [&](int cs, float (&l)[kMergeBatch], f32x4 (&v)[kMergeBatch]) {
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const int ck = cs + k * kMergeLanes;
+      const int64_t cc = ck < c1 ? ck : c1 - 1;
+      l[k] = part_lse[cc * R + r];
+      v[k] = *reinterpret_cast<const f32x4*>(obase + cc * R * kValue);
+      if (ck >= c1) l[k] = -INFINITY;
+    }
+  };
+  auto fold = [&](const float (&l)[kMergeBatch], const f32x4 (&v)[kMergeBatch]) {
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const float lt = l[k] * kLog2e;
+      const float mn = fmaxf(m, lt);
+      if (mn > -INFINITY) {
+        const float sc = __builtin_amdgcn_exp2f(m - mn);   // 0 while nothing was folded
+        const float w = __builtin_amdgcn_exp2f(lt - mn);   // 0 for an empty chunk
+        acc = acc * sc + w * v[k];
+        ws = ws * sc + w;
+        m = mn;
+      }
+    }
+  };
+  float la[kMergeBatch], lb[kMergeBatch];
+  f32x4 va[kMergeBatch], vb[kMergeBatch];
+  constexpr int kStep = kMergeBatch * kMergeLanes;
   int c = c0 + cl;
-  for (; c + 3 * kMergeLanes < c1; c += 4 * kMergeLanes) {
-    float w[4];
-    f32x4 v[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t ck = c + k * kMergeLanes;
-      w[k] = part_lse[ck * R + r];
-      v[k] = *reinterpret_cast<const f32x4*>(obase + ck * R * kValue);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float wk = __builtin_amdgcn_exp2f((w[k] - mx) * kLog2e);
-      acc += wk * v[k];
-      wsum += wk;
-    }
+  load(c, la, va);
+  for (; c < c1; c += 2 * kStep) {
+    if (c + kStep < c1) load(c + kStep, lb, vb);
+    fold(la, va);
+    if (c + kStep >= c1) break;
+    if (c + 2 * kStep < c1) load(c + 2 * kStep, la, va);
+    fold(lb, vb);
   }
-  for (; c < c1; c += kMergeLanes) {
-    const float wk = __builtin_amdgcn_exp2f((part_lse[(int64_t)c * R + r] - mx) * kLog2e);
-    acc += wk * *reinterpret_cast<const f32x4*>(obase + (int64_t)c * R * kValue);
-    wsum += wk;
-  }
+
   s_acc[cl][dl] = acc;
-  if (dl == 0) s_w[cl] = wsum;
+  if (dl == 0) {
+    s_m[cl] = m;
+    s_w[cl] = ws;
+  }
   __syncthreads();
   if (cl == 0) {
-    f32x4 tot = s_acc[0][dl];
-    float wt = s_w[0];
+    float M = s_m[0];
 #pragma unroll
-    for (int k = 1; k < kMergeLanes; ++k) {
-      tot += s_acc[k][dl];
-      wt += s_w[k];
+    for (int k = 1; k < kMergeLanes; ++k) M = fmaxf(M, s_m[k]);
+    if (!(M > -INFINITY)) {   // nothing visible in any chunk
+      *reinterpret_cast<f32x4*>(orow) = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (dl == 0 && qd == 0) lse[grow] = -INFINITY;
+      return;
+    }
+    f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+    float wt = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMergeLanes; ++k) {
+      const float sc = __builtin_amdgcn_exp2f(s_m[k] - M);   // 0 for a lane with no visible chunk
+      tot += sc * s_acc[k][dl];
+      wt += sc * s_w[k];
     }
     *reinterpret_cast<f32x4*>(orow) = tot * (1.f / wt);
-    if (dl == 0 && qd == 0) lse[grow] = mx + __builtin_amdgcn_logf(wt) * kLn2;
+    if (dl == 0 && qd == 0) lse[grow] = (M + __builtin_amdgcn_logf(wt)) * kLn2;
   }
 }
 
