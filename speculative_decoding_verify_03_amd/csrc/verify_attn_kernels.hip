@@ -86,20 +86,38 @@ __device__ __forceinline__ GatherLane gather_lane(int gw, int lane) {
   return g;
 }
 
+// Direct-to-LDS loads, written out in asm. (Issued through the builtin, an LDS
+// DMA anywhere in a wave's code makes the compiler wait for every LDS read of
+// that wave with lgkmcnt(0), draining the operand reads queued ahead of each
+// MFMA.) M0 carries the wave-uniform LDS destination and is restored after
+// the load. The loads write LDS only, so no register is left pending; their
+// completion is awaited with explicit vmcnt waits, and the compiler's own
+// vmcnt waits only grow stricter for not counting them.
+__device__ __forceinline__ void lds_dma16_nt(const char* gaddr, LDS_AS char* lds_dst) {
+  const unsigned lb = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_dst);
+  unsigned saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(gaddr), "s"(lb) : "memory");
+}
+__device__ __forceinline__ void lds_dma4(const void* gaddr, LDS_AS char* lds_dst) {
+  const unsigned lb = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_dst);
+  unsigned saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(gaddr), "s"(lb) : "memory");
+}
+
 // Issue this wave's share of one tile gather (exactly kGatherLoads load
 // instructions). `slot` is the pool row of the lane's key (any out-of-range
 // value for an absent position: zero row). The loads carry the nontemporal
-// cache policy: a workgroup reads each row once, and with it one CU sustains
-// about twice the gather rate it reaches under the default policy.
-constexpr int kGatherPolicy = 2;   // cache-policy bit nt
+// cache policy (nt): a workgroup reads each row once, and with it one CU
+// sustains about twice the gather rate it reaches under the default policy.
 __device__ __forceinline__ void issue_tile_gather(const char* kv_pool, int64_t num_slots, int32_t slot,
                                                   LDS_AS char* tile, const GatherLane& gl) {
   const char* row = (slot >= 0 && slot < num_slots) ? kv_pool + (int64_t)slot * kRowBytes
                                                     : reinterpret_cast<const char*>(g_zero_row);
   row += gl.coff;
 #pragma unroll
-  for (int L = 0; L < kGatherLoads; ++L)
-    __builtin_amdgcn_global_load_lds(row + L * 128, tile + (gl.kg * 9 + L) * 1024, 16, 0, kGatherPolicy);
+  for (int L = 0; L < kGatherLoads; ++L) lds_dma16_nt(row + L * 128, tile + (gl.kg * 9 + L) * 1024);
 }
 
 __device__ __forceinline__ LDS_AS char* lds_cast(char* p) { return (LDS_AS char*)(p); }
@@ -449,7 +467,7 @@ split_kernel(SplitArgs a) {
       int64_t gpos = sbase + kstart + (int64_t)v * kUnit + (lane & 31);
       gpos = gpos < a.total_kv ? gpos : a.total_kv - 1;
       gpos = gpos < 0 ? 0 : gpos;
-      __builtin_amdgcn_global_load_lds(a.kv_indices + gpos, slot_ring + (v % kSlotRing) * 256, 4, 0, 0);
+      lds_dma4(a.kv_indices + gpos, slot_ring + (v % kSlotRing) * 256);
     }
   };
   auto read_slot = [&](int v) -> int32_t {
@@ -481,8 +499,8 @@ split_kernel(SplitArgs a) {
   // O^T *= alpha(v) when some row's running max grew in tile v (rare); rows
   // whose max did not grow carry alpha = 1.
   auto rescale = [&](int v) {
-    const i32x4 flags = *reinterpret_cast<LDS_AS const i32x4*>(fbuf_of(v));
-    if (flags[0] | flags[1] | flags[2] | flags[3]) {
+    const uint32_t flags = *reinterpret_cast<LDS_AS const uint32_t*>(fbuf_of(v));   // one byte per pair
+    if (flags) {
 #pragma unroll
       for (int rb = 0; rb < kRowBlocks; ++rb) {
         const float al = *reinterpret_cast<LDS_AS const float*>(abuf_of(v) + (rb * 32 + n) * 4);
@@ -500,6 +518,9 @@ split_kernel(SplitArgs a) {
       d[1] = *reinterpret_cast<LDS_AS const f16x8*>(pbuf_of(v) + rb * kPBytes + 1024);
     };
     pload(0, pb[0]);
+    // O^T *= alpha(v) first; the flag read queues behind the first P reads,
+    // so both arrive in one LDS round trip.
+    rescale(v);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb) {
@@ -604,7 +625,7 @@ split_kernel(SplitArgs a) {
     *reinterpret_cast<LDS_AS f16x8*>(pbuf_of(u) + pair * kPBytes + 1024) = p1;
     const int any_grow = __ballot(grow) != 0;  // wave-wide: taken before any lane is masked off
     if (h == 0) *reinterpret_cast<LDS_AS float*>(abuf_of(u) + (pair * 32 + n) * 4) = alpha;
-    if (lane == 0) *reinterpret_cast<LDS_AS int*>(fbuf_of(u) + pair * 4) = any_grow;
+    if (lane == 0) *reinterpret_cast<LDS_AS uint8_t*>(fbuf_of(u) + pair) = (uint8_t)any_grow;
   };
   // ---- this wave's value operands of one tile: V^T for its two 32-dim
   // blocks and both 16-key steps, transposed and converted to fp16.
@@ -706,13 +727,15 @@ split_kernel(SplitArgs a) {
       if constexpr (PP == 0) {
         softmax(u, sa);
       } else {
-        if (u > 0) {
-          rescale(u - 1);
-          apply_values(u - 1, vheld);
-        }
+        // The wave feeding the matrix core raises its issue priority for
+        // its MFMA stretch, so that the other wave of its SIMD yields to
+        // its operand reads.
+        __builtin_amdgcn_s_setprio(1);
+        if (u > 0) apply_values(u - 1, vheld);
         // (the else branch keeps the old block from living on through the MFMAs)
         if (more) sa = scores(next);
         else sa = f32x16{};
+        __builtin_amdgcn_s_setprio(0);
       }
       f16x8 va[kWaveDvBlocks][2];
       read_values(tile, va);
@@ -721,12 +744,13 @@ split_kernel(SplitArgs a) {
 
       // ---- phase X
       if constexpr (PP == 0) {
-        rescale(u);
+        __builtin_amdgcn_s_setprio(1);   // as in the odd half's phase Y
         apply_values(u, va);
         // Unconditional (after the last tile this reads a landed tile of zero
         // rows and the result is dropped): a conditional update keeps the old
         // block live through the MFMAs, and the registers do not allow it.
         sa = scores(next);
+        __builtin_amdgcn_s_setprio(0);
         asm volatile("s_barrier" ::: "memory");
       } else {
 #pragma unroll
@@ -749,7 +773,6 @@ split_kernel(SplitArgs a) {
     }
     // the odd half's value update of the last tile
     if constexpr (PP == 1) {
-      rescale(nunits - 1);
       apply_values(nunits - 1, vheld);
     }
   };
@@ -766,7 +789,9 @@ split_kernel(SplitArgs a) {
     if (p == 0) {
       if (h == 0) *reinterpret_cast<LDS_AS float*>(abuf + (pair * 32 + n) * 4) = live ? 1.f / l_tot : 0.f;
       const float lse_v = live ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-      if (row_ok && h == 0) a.part_lse[(int64_t)c * a.R + r] = lse_v;
+      // the row index is re-derived here rather than kept live through the loop
+      const int r2 = rt * kRowsPerWG + pair * 32 + (fresh_lane() & 31);
+      if (r2 < a.R && h == 0) a.part_lse[(int64_t)c * a.R + r2] = lse_v;
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     // The normalised block goes out through a wave-private LDS staging area
