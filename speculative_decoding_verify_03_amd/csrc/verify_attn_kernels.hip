@@ -629,13 +629,9 @@ split_kernel(SplitArgs a) {
   };
   // ---- this wave's value operands of one tile: V^T for its two 32-dim
   // blocks and both 16-key steps, transposed and converted to fp16.
-  // The eight transpose reads and their wait form one asm statement, so the
-  // outputs are complete when it ends. (As separate builtins the compiler
-  // fences each with vmcnt(0) against the direct-to-LDS loads in flight, which
-  // would drain the gathers; split into an asm read plus a later wait, the
-  // compiler may copy a destination register before the data has arrived.)
-  // The leading s_nop keeps the new register writes clear of operand reads of
-  // MFMAs still in flight.
+  // The transpose reads are compiler builtins, so their waits are counted
+  // like any other LDS read (the direct-to-LDS loads, being asm, do not make
+  // the compiler fence them).
   auto read_values = [&](LDS_AS const char* tile, f16x8 (&va)[kWaveDvBlocks][2]) {
     u32x2 v[kWaveDvBlocks][2][2];   // [d][t][hf]
     int tr_off[2][2];
@@ -644,21 +640,18 @@ split_kernel(SplitArgs a) {
     const unsigned a10 = (unsigned)(uintptr_t)(tile + tr_off[1][0]);
     const unsigned a01 = (unsigned)(uintptr_t)(tile + tr_off[0][1]);
     const unsigned a11 = (unsigned)(uintptr_t)(tile + tr_off[1][1]);
-    asm volatile(
-        "s_nop 7\n\t"
-        "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %9\n\t"
-        "ds_read_b64_tr_b16 %2, %8 offset:18432\n\t"
-        "ds_read_b64_tr_b16 %3, %9 offset:18432\n\t"
-        "ds_read_b64_tr_b16 %4, %10\n\t"
-        "ds_read_b64_tr_b16 %5, %11\n\t"
-        "ds_read_b64_tr_b16 %6, %10 offset:18432\n\t"
-        "ds_read_b64_tr_b16 %7, %11 offset:18432\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(v[0][0][0]), "=&v"(v[0][0][1]), "=&v"(v[0][1][0]), "=&v"(v[0][1][1]),
-          "=&v"(v[1][0][0]), "=&v"(v[1][0][1]), "=&v"(v[1][1][0]), "=&v"(v[1][1][1])
-        : "v"(a00), "v"(a10), "v"(a01), "v"(a11)
-        : "memory");
+    auto tr = [&](unsigned addr) {
+      const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(uintptr_t)addr);
+      return __builtin_bit_cast(u32x2, r);
+    };
+    v[0][0][0] = tr(a00);
+    v[0][0][1] = tr(a10);
+    v[0][1][0] = tr(a00 + 18432);
+    v[0][1][1] = tr(a10 + 18432);
+    v[1][0][0] = tr(a01);
+    v[1][0][1] = tr(a11);
+    v[1][1][0] = tr(a01 + 18432);
+    v[1][1][1] = tr(a11 + 18432);
 #pragma unroll
     for (int db = 0; db < kWaveDvBlocks; ++db)
 #pragma unroll
@@ -739,6 +732,14 @@ split_kernel(SplitArgs a) {
       }
       f16x8 va[kWaveDvBlocks][2];
       read_values(tile, va);
+      if constexpr (PP == 0) {
+        // The even wave converts its values before the barrier: its phase Y
+        // has slack, its phase X does not. (The odd wave's conversion is left
+        // to the compiler, which sinks it into phase X, where the odd wave
+        // has slack.)
+#pragma unroll
+        for (int db = 0; db < kWaveDvBlocks; ++db) asm volatile("" ::"v"(va[db][0]), "v"(va[db][1]));
+      }
       // P/alpha/flag stores of the even half are complete before the barrier
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
