@@ -511,28 +511,31 @@ split_kernel(SplitArgs a) {
   };
   // O^T += V(v)^T P(v)^T for this wave's 64 dims and all 128 rows.
   auto apply_values = [&](int v, const f16x8 (&va)[kWaveDvBlocks][2]) {
-    // P operands are read one row block ahead of their MFMAs
-    f16x8 pb[2][2];
-    auto pload = [&](int rb, f16x8 (&d)[2]) {
-      d[0] = *reinterpret_cast<LDS_AS const f16x8*>(pbuf_of(v) + rb * kPBytes);
-      d[1] = *reinterpret_cast<LDS_AS const f16x8*>(pbuf_of(v) + rb * kPBytes + 1024);
+    // MFMA pair i (of 8) takes P(row block i % 4, key step i / 4). The P
+    // operands stream through a ring of three reads: the read for pair i+3 is
+    // issued right after pair i, two pairs of MFMAs ahead of its use.
+    // Consecutive MFMAs write different accumulators.
+    constexpr int kPRing = 3;
+    auto pread = [&](int i) {
+      return *reinterpret_cast<LDS_AS const f16x8*>(pbuf_of(v) + (i % kRowBlocks) * kPBytes + (i / kRowBlocks) * 1024);
     };
-    pload(0, pb[0]);
+    f16x8 pq[kPRing];
+    pq[0] = pread(0);
+    pq[1] = pread(1);
     // O^T *= alpha(v) first; the flag read queues behind the first P reads,
-    // so both arrive in one LDS round trip.
+    // so they arrive in one LDS round trip.
     rescale(v);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int rb = 0; rb < kRowBlocks; ++rb) {
-      if (rb + 1 < kRowBlocks) pload(rb + 1, pb[(rb + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-      // key step outer, so consecutive MFMAs are independent
+    for (int i = 2; i < kPRing; ++i) pq[i] = pread(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 2 * kRowBlocks; ++i) {
+      const int rb = i % kRowBlocks, t = i / kRowBlocks;
 #pragma unroll
       for (int db = 0; db < kWaveDvBlocks; ++db)
-        o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[db][0], pb[rb & 1][0], o[rb][db], 0, 0, 0);
-#pragma unroll
-      for (int db = 0; db < kWaveDvBlocks; ++db)
-        o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[db][1], pb[rb & 1][1], o[rb][db], 0, 0, 0);
+        o[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[db][t], pq[i % kPRing], o[rb][db], 0, 0, 0);
+      if (i + kPRing < 2 * kRowBlocks) pq[i % kPRing] = pread(i + kPRing);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
