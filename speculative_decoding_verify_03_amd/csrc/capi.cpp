@@ -96,7 +96,7 @@ bool make_plan(int B, int Q, int H, int64_t total_kv, int ncu, va::Plan* p) {
   off += sizeof(float) * (size_t)max_chunks * (size_t)R;
   off = align_up(off, 256);
   p->off_o = off;
-  off += sizeof(float) * (size_t)max_chunks * (size_t)R * va::kValue;
+  off += sizeof(uint16_t) * (size_t)max_chunks * (size_t)R * va::kValue;   // fp16 partial outputs
   p->bytes = align_up(off, 256);
   return true;
 }
@@ -161,7 +161,7 @@ int verify_attn(const void* q, const void* kv_pool, const int32_t* kv_indices,
     char* ws = static_cast<char*>(workspace);
     auto* chunk_off = reinterpret_cast<int32_t*>(ws + p.off_chunk);
     auto* part_lse = reinterpret_cast<float*>(ws + p.off_lse);
-    auto* part_o = reinterpret_cast<float*>(ws + p.off_o);
+    auto* part_o = reinterpret_cast<_Float16*>(ws + p.off_o);
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
 

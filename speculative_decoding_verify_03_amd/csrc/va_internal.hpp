@@ -39,7 +39,7 @@ struct SplitArgs {
   const int32_t* prefix_lens;
   const uint8_t* tree_mask;
   int32_t* chunk_off;      // written by workgroup 0: [B + 1] chunk offsets for the merge
-  float* part_o;
+  _Float16* part_o;       // [max_chunks][R][512] fp16, normalised (O / l)
   float* part_lse;
   int64_t num_slots;
   int64_t total_kv;
@@ -49,7 +49,7 @@ struct SplitArgs {
 };
 
 hipError_t launch_split(const SplitArgs& a, int grid, hipStream_t stream);
-hipError_t launch_merge(const float* part_o, const float* part_lse, const int32_t* chunk_off,
+hipError_t launch_merge(const _Float16* part_o, const float* part_lse, const int32_t* chunk_off,
                         float* out, float* lse, int B, int R, hipStream_t stream);
 hipError_t launch_debug_gather(const void* kv_pool, const int32_t* kv_indices, int64_t n,
                                int64_t num_slots, void* rows_out, hipStream_t stream);

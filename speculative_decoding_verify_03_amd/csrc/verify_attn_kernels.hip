@@ -39,6 +39,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -328,9 +329,10 @@ static_assert(kSplitLds <= 160 * 1024, "split kernel LDS budget");
 // their tile.
 static_assert(kSlotAhead - 2 >= kGatherAhead, "slot copy distance");
 static_assert(kSlotRing > kSlotAhead && kGatherAhead == kRingS, "ring sizes");
-// Epilogue staging: one 32-row block of a wave's 64 dims, rows padded to 272
-// bytes, per wave, inside the tile ring.
-constexpr int kStageRow = kWaveDvBlocks * 32 * 4 + 16;
+// Epilogue staging: one 32-row block of a wave's 64 dims in fp16, rows padded
+// to 144 bytes (a multiple of 16, for the 16-byte read-back), per wave, inside
+// the tile ring.
+constexpr int kStageRow = kWaveDvBlocks * 32 * 2 + 16;
 constexpr int kStageBytes = 32 * kStageRow;
 static_assert(kSplitWaves * kStageBytes <= kOffXchg, "epilogue staging fits in the tile ring");
 
@@ -798,11 +800,12 @@ split_kernel(SplitArgs a) {
       if (r2 < a.R && h == 0) a.part_lse[(int64_t)c * a.R + r2] = lse_v;
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // The normalised block goes out through a wave-private LDS staging area
-    // (the tile ring is free now): written in the accumulator layout, read
-    // back row-major, so that every store instruction writes four rows of 256
-    // contiguous bytes (whole 128-byte lines) instead of 32-byte pieces of 32
-    // rows. Rows are padded to 272 bytes against bank conflicts.
+    // The normalised block is rounded to fp16 (|O / l| is at most the largest
+    // |value| in the chunk, which the fp16 value operands already bound) and
+    // goes out through a wave-private LDS staging area (the tile ring is free
+    // now): written in the accumulator layout, read back row-major, so that
+    // every store instruction writes eight rows of 128 contiguous bytes
+    // (whole lines) instead of 8-byte pieces of 32 rows.
     LDS_AS char* stg = lds + wave * kStageBytes;
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb) {
@@ -810,18 +813,20 @@ split_kernel(SplitArgs a) {
 #pragma unroll
       for (int db = 0; db < kWaveDvBlocks; ++db)
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-          *reinterpret_cast<LDS_AS f32x4*>(stg + n * kStageRow + (db * 32 + 8 * qd + 4 * h) * 4) =
-              f32x4{o[rb][db][4 * qd] * inv, o[rb][db][4 * qd + 1] * inv, o[rb][db][4 * qd + 2] * inv,
-                    o[rb][db][4 * qd + 3] * inv};
+        for (int qd = 0; qd < 4; ++qd) {
+          f16x4 hv;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int row = 4 * k + (lane >> 4);
-        const int ch = lane & 15;
-        const f32x4 v = *reinterpret_cast<LDS_AS const f32x4*>(stg + row * kStageRow + ch * 16);
+          for (int e = 0; e < 4; ++e) hv[e] = (_Float16)(o[rb][db][4 * qd + e] * inv);
+          *reinterpret_cast<LDS_AS f16x4*>(stg + n * kStageRow + (db * 32 + 8 * qd + 4 * h) * 2) = hv;
+        }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int row = 8 * k + (lane >> 3);
+        const int ch = lane & 7;
+        const u32x4 v = *reinterpret_cast<LDS_AS const u32x4*>(stg + row * kStageRow + ch * 16);
         const int rw = rt * kRowsPerWG + rb * 32 + row;
         if (rw < a.R)
-          *reinterpret_cast<f32x4*>(a.part_o + ((int64_t)c * a.R + rw) * kValue + wave * kWaveDvBlocks * 32 + ch * 4) = v;
+          *reinterpret_cast<u32x4*>(a.part_o + ((int64_t)c * a.R + rw) * kValue + wave * kWaveDvBlocks * 32 + ch * 8) = v;
       }
     }
   }
@@ -831,7 +836,7 @@ split_kernel(SplitArgs a) {
 // Merge: lse = ln sum_s exp(lse_s); out = sum_s exp(lse_s - lse) O_s.
 // One 256-thread workgroup per (row, quarter of the 512 value dims): thread
 // t handles 4 dims (t % 32) of the quarter for chunks c0 + (t / 32) + 8k, so
-// each wave reads two whole 512-byte row segments per step and the chunks
+// each wave reads two whole 256-byte fp16 row segments per step and the chunks
 // of a row are spread over 8 lanes. Each lane folds its chunks in one pass
 // with a running maximum (the log2 domain; earlier terms are rescaled when it
 // grows), loading the next four chunks while it folds the current four; an
@@ -840,7 +845,7 @@ split_kernel(SplitArgs a) {
 constexpr int kMergeLanes = 8;   // chunk lanes per workgroup
 constexpr int kMergeBatch = 4;   // chunks per lane and load batch
 
-__global__ void __launch_bounds__(256) merge_kernel(const float* __restrict__ part_o,
+__global__ void __launch_bounds__(256) merge_kernel(const _Float16* __restrict__ part_o,
                                                     const float* __restrict__ part_lse,
                                                     const int32_t* __restrict__ chunk_off,
                                                     float* __restrict__ out, float* __restrict__ lse,
@@ -867,7 +872,7 @@ __global__ void __launch_bounds__(256) merge_kernel(const float* __restrict__ pa
   // lane's chunks. Chunks that are empty for the row (lse_s = -inf) weigh 0.
   float m = -INFINITY, ws = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const float* obase = part_o + (int64_t)r * kValue + qd * 128 + 4 * dl;
+  const _Float16* obase = part_o + (int64_t)r * kValue + qd * 128 + 4 * dl;
   // Batch of chunks cs + 8k; positions past the row's last chunk load that
   // chunk again and count as empty.
   auto load = [&](int cs, float (&l)[kMergeBatch], f32x4 (&v)[kMergeBatch]) {
@@ -876,7 +881,8 @@ __global__ void __launch_bounds__(256) merge_kernel(const float* __restrict__ pa
       const int ck = cs + k * kMergeLanes;
       const int64_t cc = ck < c1 ? ck : c1 - 1;
       l[k] = part_lse[cc * R + r];
-      v[k] = *reinterpret_cast<const f32x4*>(obase + cc * R * kValue);
+      const f16x4 hv = *reinterpret_cast<const f16x4*>(obase + cc * R * kValue);
+      v[k] = f32x4{(float)hv[0], (float)hv[1], (float)hv[2], (float)hv[3]};
       if (ck >= c1) l[k] = -INFINITY;
     }
   };
@@ -969,7 +975,7 @@ hipError_t launch_split(const SplitArgs& a, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const float* part_o, const float* part_lse, const int32_t* chunk_off,
+hipError_t launch_merge(const _Float16* part_o, const float* part_lse, const int32_t* chunk_off,
                         float* out, float* lse, int B, int R, hipStream_t stream) {
   const int64_t rows = (int64_t)B * R;
   hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(rows * 4)), dim3(256), 0, stream, part_o,
