@@ -671,12 +671,13 @@ split_kernel(SplitArgs a) {
   // core:
   //   phase Y: the even wave runs the softmax of tile u (vector ALU) while the
   //            odd wave applies tile u-1 to its values and computes its
-  //            partial scores of tile u+1 (34 MFMAs); both then read their
-  //            value operands of tile u, which frees tile u's ring slot;
+  //            partial scores of tile u+1 (34 MFMAs); the even wave then
+  //            reads its value operands of tile u;
   //   phase X: the even wave applies tile u and computes its partial scores
-  //            of tile u+1 (34 MFMAs) while the odd wave hands over its
-  //            partial scores, issues the gather of tile u+3 into the freed
-  //            slot, and waits for tile u+2.
+  //            of tile u+1 (34 MFMAs) while the odd wave reads its value
+  //            operands of tile u (which frees tile u's ring slot), hands over
+  //            its partial scores, issues the gather of tile u+3 into the
+  //            freed slot, and waits for tile u+2.
   // P, the rescale factors and flags are double-buffered by tile parity, as
   // the odd half reads those of tile u-1 while the even half writes tile u's.
   auto run = [&](auto pc) {
@@ -736,12 +737,11 @@ split_kernel(SplitArgs a) {
         __builtin_amdgcn_s_setprio(0);
       }
       f16x8 va[kWaveDvBlocks][2];
-      read_values(tile, va);
+      if constexpr (PP == 0) read_values(tile, va);
       if constexpr (PP == 0) {
         // The even wave converts its values before the barrier: its phase Y
-        // has slack, its phase X does not. (The odd wave's conversion is left
-        // to the compiler, which sinks it into phase X, where the odd wave
-        // has slack.)
+        // has slack, its phase X does not. (The odd wave reads and converts
+        // its values of tile u in phase X, where it has slack.)
 #pragma unroll
         for (int db = 0; db < kWaveDvBlocks; ++db) asm volatile("" ::"v"(va[db][0]), "v"(va[db][1]));
       }
@@ -759,15 +759,14 @@ split_kernel(SplitArgs a) {
         __builtin_amdgcn_s_setprio(0);
         asm volatile("s_barrier" ::: "memory");
       } else {
-#pragma unroll
-        for (int db = 0; db < kWaveDvBlocks; ++db) {
-          vheld[db][0] = va[db][0];
-          vheld[db][1] = va[db][1];
-        }
+        // the odd wave reads its values of tile u here, where it has slack
+        read_values(tile, vheld);
         if (more) write_xchg(sa);
         load_slots_to_lds(u + kSlotAhead);
         const int32_t slot = read_slot(u + kGatherAhead);
-        issue(slot, tile);   // nobody reads tile u any more
+        // nobody reads tile u any more once this wave's value reads are done
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue(slot, tile);
         // Tile u+2 has landed once no more than the loads issued after it are
         // outstanding: this phase's slot copy (wave 4) and its nine gather
         // loads. (The compiler does not track direct-to-LDS loads, so the wait
