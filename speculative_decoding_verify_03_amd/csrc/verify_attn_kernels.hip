@@ -25,7 +25,9 @@
 //    accumulator layout itself (published through LDS), V^T is read from the
 //    same LDS tile with the gfx950 transpose read ds_read_b64_tr_b16 and
 //    converted bf16 -> fp16 in registers. P is fp16 (not bf16) for accuracy:
-//    fp16 keeps 11 significant bits against bf16's 8.
+//    fp16 keeps 11 significant bits against bf16's 8;
+//  * partials: each chunk leaves O / l in fp16 (bounded by the largest |value|
+//    of the chunk) and its lse in fp32; the merge folds them in fp32.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
