@@ -282,3 +282,35 @@ def test_defragmented_cache_full_size_bitwise_equal(env):
     o1, l1 = run_gpu(va, upload(w1), w1.scale)
     o2, l2 = run_gpu(va, upload(w2), w2.scale)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def _scale_bf16(bits, s):
+    """bf16 bit patterns times a power of two (exact in bf16 for these magnitudes)."""
+    f = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32) * np.float32(s)
+    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def test_scale_equivariance_large_values(env):
+    """Latents times 16 and queries times 1/16 leave every score unchanged and scale
+    out by 16 exactly, lse not at all. The relative error must stay within the bar
+    and the absolute error may grow with the values (here |v| up to about 100):
+    the value operands and the chunk partials are fp16, whose rounding is relative
+    to the magnitude."""
+    s = 16.0
+    w = make_workload("big", [306], B=2, Q=8, H=16, prefix_lens=[700, 1500], mask="tree", num_slots=3000)
+    w.kv_pool = _scale_bf16(w.kv_pool, s)
+    w.q = _scale_bf16(w.q, 1.0 / s)
+    torch, va = env
+    out, lse = run_gpu(va, upload(w), w.scale)
+    ro, rl = _oracle(w)
+    assert np.isfinite(ro).all() and np.isfinite(rl).all()
+    rel = float(np.linalg.norm(out - ro) / np.linalg.norm(ro))
+    mabs = float(np.abs(out - ro).max())
+    labs = float(np.abs(lse - rl).max())
+    print(f"[parity] scaled x{s:g}: rel_l2={rel:.3e} max_abs={mabs:.3e} lse_abs={labs:.3e}", flush=True)
+    assert rel <= 1e-3 and mabs <= s * 5e-3 and labs <= 1e-3
+    # the same inputs unscaled give out / 16 up to rounding of the same size, relatively
+    w0 = make_workload("big", [306], B=2, Q=8, H=16, prefix_lens=[700, 1500], mask="tree", num_slots=3000)
+    out0, lse0 = run_gpu(va, upload(w0), w0.scale)
+    assert float(np.linalg.norm(out / s - out0) / np.linalg.norm(out0)) <= 1e-3
+    assert float(np.abs(lse - lse0).max()) <= 1e-3
