@@ -14,7 +14,7 @@ constexpr int kUnit = 32;              // keys per LDS tile
 constexpr int kRowsPerBlock = 32;      // query-head rows of one 32x32 MFMA score block
 constexpr int kRowBlocksPerWG = 4;     // score blocks per workgroup (one per wave pair)
 constexpr int kRowsPerWG = kRowsPerBlock * kRowBlocksPerWG;  // 128 rows per row tile
-constexpr int kMinChunk = 256;         // smallest chunk worth a workgroup (keys)
+constexpr int kMinChunk = 128;         // smallest chunk worth a workgroup (keys): four tiles
 
 // Host-side split plan (the split kernel picks the chunk length from the
 // sequence lengths: the shortest one, not below ideal_keys, that needs at

@@ -91,7 +91,7 @@ def test_plan_shapes(lib):
     assert p["grid"] % 8 == 0 and p["grid"] >= p["row_tiles"]
     assert p["max_chunks"] >= (185016 + p["chunk_keys"] - 1) // p["chunk_keys"]
     p1 = va.query_plan(1, 4, 8, 260)
-    assert p1["row_tiles"] == 1 and p1["chunk_keys"] == 256   # floor of 256 keys per chunk
+    assert p1["row_tiles"] == 1 and p1["chunk_keys"] == 128   # floor of 128 keys per chunk
     va.set_chunk_override(64)
     assert va.query_plan(1, 4, 8, 260)["chunk_keys"] == 64
     va.set_chunk_override(0)
