@@ -192,7 +192,7 @@ int verify_attn(const void* q, const void* kv_pool, const int32_t* kv_indices,
     if (g_split_stop != nullptr && (e = hipEventRecord(g_split_stop, st)) != hipSuccess)
       return fail(VA_EHIP, "event record: %s", hipGetErrorString(e));
 
-    e = va::launch_merge(part_o, part_lse, chunk_off, out, lse, B, Q * H, st);
+    e = va::launch_merge(part_o, part_lse, chunk_off, out, lse, B, Q * H, p.max_chunks, st);
     if (e != hipSuccess) return fail(VA_EHIP, "merge launch: %s", hipGetErrorString(e));
     return ok();
   } catch (...) {

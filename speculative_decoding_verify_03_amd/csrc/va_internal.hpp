@@ -49,8 +49,11 @@ struct SplitArgs {
 };
 
 hipError_t launch_split(const SplitArgs& a, int grid, hipStream_t stream);
+// The merge: the one-wave-per-row form when the partial buffers hold at most
+// kMergeFewPerSeq chunks per sequence on average, else the chunk-lane form.
+constexpr int kMergeFewPerSeq = 16;
 hipError_t launch_merge(const _Float16* part_o, const float* part_lse, const int32_t* chunk_off,
-                        float* out, float* lse, int B, int R, hipStream_t stream);
+                        float* out, float* lse, int B, int R, int max_chunks, hipStream_t stream);
 hipError_t launch_debug_gather(const void* kv_pool, const int32_t* kv_indices, int64_t n,
                                int64_t num_slots, void* rows_out, hipStream_t stream);
 hipError_t launch_defrag(const void* src_pool, const int32_t* kv_indices, int64_t n, int64_t num_slots,

@@ -943,6 +943,69 @@ __global__ void __launch_bounds__(256) merge_kernel(const _Float16* __restrict__
 }
 
 // ---------------------------------------------------------------------------
+// Merge for batches whose sequences have few chunks each: one wave per (row,
+// half of the 512 value dims), lane l holding 4 dims, with no cross-lane
+// step. The wave loads the partials of up to eight chunks at once and folds
+// them with a running maximum (log2 domain), batch after batch, so any number
+// of chunks is handled; with few chunks per row this keeps every loaded byte
+// useful and the grid small, where the chunk-lane merge above would leave
+// most of its lanes idle.
+// ---------------------------------------------------------------------------
+constexpr int kFewBatch = 8;
+
+__global__ void __launch_bounds__(256) merge_few_kernel(const _Float16* __restrict__ part_o,
+                                                        const float* __restrict__ part_lse,
+                                                        const int32_t* __restrict__ chunk_off,
+                                                        float* __restrict__ out, float* __restrict__ lse,
+                                                        int B, int R) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (row, half)
+  if (item >= (int64_t)B * R * 2) return;   // uniform per wave
+  const int64_t grow = item >> 1;
+  const int half = (int)(item & 1);
+  const int b = (int)(grow / R);
+  const int r = (int)(grow - (int64_t)b * R);
+  const int c0 = chunk_off[b], c1 = chunk_off[b + 1];
+  float* orow = out + grow * kValue + half * 256 + 4 * lane;
+  const _Float16* obase = part_o + (int64_t)r * kValue + half * 256 + 4 * lane;
+  float m = -INFINITY, ws = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int cs = c0; cs < c1; cs += kFewBatch) {
+    float l[kFewBatch];
+    f16x4 v[kFewBatch];
+#pragma unroll
+    for (int k = 0; k < kFewBatch; ++k) {
+      const int ck = cs + k;
+      const int64_t cc = ck < c1 ? ck : c1 - 1;   // past the row's last chunk: reload it, weigh 0
+      l[k] = ck < c1 ? part_lse[cc * R + r] * kLog2e : -INFINITY;
+      v[k] = *reinterpret_cast<const f16x4*>(obase + cc * R * kValue);
+    }
+    float mb = m;
+#pragma unroll
+    for (int k = 0; k < kFewBatch; ++k) mb = fmaxf(mb, l[k]);
+    if (mb > -INFINITY) {
+      const float sc = __builtin_amdgcn_exp2f(m - mb);   // 0 while nothing was folded
+      acc *= sc;
+      ws *= sc;
+#pragma unroll
+      for (int k = 0; k < kFewBatch; ++k) {
+        const float w = __builtin_amdgcn_exp2f(l[k] - mb);   // 0 for an empty chunk
+        acc += w * f32x4{(float)v[k][0], (float)v[k][1], (float)v[k][2], (float)v[k][3]};
+        ws += w;
+      }
+      m = mb;
+    }
+  }
+  if (!(m > -INFINITY)) {   // no chunk, or nothing visible in any chunk
+    *reinterpret_cast<f32x4*>(orow) = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (lane == 0 && half == 0) lse[grow] = -INFINITY;
+    return;
+  }
+  *reinterpret_cast<f32x4*>(orow) = acc * (1.f / ws);
+  if (lane == 0 && half == 0) lse[grow] = (m + __builtin_amdgcn_logf(ws)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
 // Debug gather: the split kernel's gather routine, copied back out in order.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(kGatherWaves * 64) debug_gather_kernel(const char* __restrict__ kv_pool,
@@ -977,10 +1040,15 @@ hipError_t launch_split(const SplitArgs& a, int grid, hipStream_t stream) {
 }
 
 hipError_t launch_merge(const _Float16* part_o, const float* part_lse, const int32_t* chunk_off,
-                        float* out, float* lse, int B, int R, hipStream_t stream) {
+                        float* out, float* lse, int B, int R, int max_chunks, hipStream_t stream) {
   const int64_t rows = (int64_t)B * R;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(rows * 4)), dim3(256), 0, stream, part_o,
-                     part_lse, chunk_off, out, lse, B, R);
+  if (max_chunks <= kMergeFewPerSeq * B) {   // few chunks per sequence on average
+    hipLaunchKernelGGL(merge_few_kernel, dim3((unsigned)((rows * 2 + 3) / 4)), dim3(256), 0, stream, part_o,
+                       part_lse, chunk_off, out, lse, B, R);
+  } else {
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(rows * 4)), dim3(256), 0, stream, part_o,
+                       part_lse, chunk_off, out, lse, B, R);
+  }
   return hipGetLastError();
 }
 
