@@ -68,26 +68,46 @@ __device__ __forceinline__ int tile_offset(int chunk, int key) {
   return ((key >> 3) * 9 + (chunk >> 3)) * 1024 + ((key & 7) * 8 + ((chunk & 7) ^ ((key >> 1) & 7))) * 16;
 }
 
-// The gather is line-granular and done by four waves: gathering wave j fetches
-// key group j (8 keys), all nine 128-byte lines of each of those rows; lane l
-// reads key 8j + l/8 and, of every line, the 16-byte chunk that lands in slot l
-// of the line's region. Every load instruction thus fetches 8 whole lines.
+// The gather is line-granular and done by four waves, nine load instructions
+// each per tile. One instruction fills one 1 KiB region (key group kg, line L):
+// lane l fetches, of key 8kg + l/8, the 16-byte chunk of line L that lands in
+// slot l%8 of the region, so every instruction moves 8 whole 128-byte lines.
+// Region ownership (gather wave j = 0..3):
+//   loads 0..4: key group j, lines 0, 1, 2, 3 and 8;
+//   loads 5..8: line 4 + j of key groups 0..3.
+// In the split kernel a tile slot is refilled while the previous tile's value
+// lines 4..7 may still be read, each by one wave only (value_line below); the
+// ownership above gives each of those lines to the wave that reads it, so
+// every refill waits for the reads of its own wave alone. The check after the
+// split kernel's layout constants proves this over the tables below.
 constexpr int kGatherWaves = kUnit / 8;
 constexpr int kGatherLoads = kRowBytes / 128;   // 9 load instructions per wave and tile
+constexpr int kKeyGroups = kUnit / 8;           // 4 groups of 8 keys per tile
+constexpr int kOwnLoads = 5;                    // loads 0..4 of gather wave j: key group j
+static_assert(kGatherWaves == kKeyGroups && kGatherLoads == kOwnLoads + kKeyGroups, "gather split");
 
-struct GatherLane {
-  int key;   // key of the tile this lane fetches
-  int coff;  // byte offset of its chunk inside a 128-byte line
-  int kg;    // key group (region row)
-};
-
-__device__ __forceinline__ GatherLane gather_lane(int gw, int lane) {
-  GatherLane g;
-  g.kg = gw;
-  g.key = 8 * gw + (lane >> 3);
-  g.coff = ((lane & 7) ^ ((g.key >> 1) & 7)) * 16;
-  return g;
+__host__ __device__ constexpr int gather_kg(int j, int k) { return k < kOwnLoads ? j : k - kOwnLoads; }
+__host__ __device__ constexpr int gather_line(int j, int k) {
+  return k < 4 ? k : (k == 4 ? kGatherLoads - 1 : 4 + j);
 }
+// Line of a tile whose value operands wave w reads (its 64 value dims are
+// chunks 8w .. 8w + 7; see value_chunk).
+__host__ __device__ constexpr int value_line(int w) { return w; }
+// Value chunk read by lane (g = lane/16, s = lane%16) of wave w for value
+// block d of that wave.
+__host__ __device__ constexpr int value_chunk(int w, int d, int g, int s) {
+  return 8 * value_line(w) + 4 * d + 2 * (g & 1) + ((s & 3) >> 1);
+}
+
+// Slot indices of a tile reach LDS through one 4-byte direct load per lane:
+// lane l < 32 fetches the index of key slot_copy_key(l) to byte 4l of the
+// tile's 256-byte ring entry (lanes 32..63 repeat lanes 0..31 into bytes
+// 128..255), so that bytes 16r .. 16r+15 hold keys r, 8 + r, 16 + r, 24 + r:
+// one 16-byte read gives a gathering lane the slots of its key in all four
+// key groups.
+__host__ __device__ constexpr int slot_copy_key(int lane) { return 8 * (lane & 3) + ((lane & 31) >> 2); }
+
+typedef int i32x4g __attribute__((ext_vector_type(4)));
 
 // Direct-to-LDS loads, written out in asm. (Issued through the builtin, an LDS
 // DMA anywhere in a wave's code makes the compiler wait for every LDS read of
@@ -109,18 +129,29 @@ __device__ __forceinline__ void lds_dma4(const void* gaddr, LDS_AS char* lds_dst
                : "=&s"(saved) : "v"(gaddr), "s"(lb) : "memory");
 }
 
-// Issue this wave's share of one tile gather (exactly kGatherLoads load
-// instructions). `slot` is the pool row of the lane's key (any out-of-range
-// value for an absent position: zero row). The loads carry the nontemporal
-// cache policy (nt): a workgroup reads each row once, and with it one CU
-// sustains about twice the gather rate it reaches under the default policy.
-__device__ __forceinline__ void issue_tile_gather(const char* kv_pool, int64_t num_slots, int32_t slot,
-                                                  LDS_AS char* tile, const GatherLane& gl) {
-  const char* row = (slot >= 0 && slot < num_slots) ? kv_pool + (int64_t)slot * kRowBytes
-                                                    : reinterpret_cast<const char*>(g_zero_row);
-  row += gl.coff;
+// Issue gather wave j's share of one tile gather (exactly kGatherLoads load
+// instructions, regions as in gather_kg / gather_line). slots[kg] is the pool
+// row of this lane's key 8kg + lane/8 (any out-of-range value for an absent
+// position: the zero row). The loads carry the nontemporal cache policy (nt):
+// a workgroup reads each row once, and with it one CU sustains about twice
+// the gather rate it reaches under the default policy.
+__device__ __forceinline__ void issue_tile_gather(const char* kv_pool, int64_t num_slots, i32x4g slots,
+                                                  LDS_AS char* tile, int j, int lane) {
+  const int r = lane >> 3, s = lane & 7;
+  // Chunk of the line that lands in slot s of a region: s ^ ((key >> 1) & 7)
+  // with key = 8kg + r, i.e. s ^ (4 (kg & 1) + r / 2).
+  auto row_of = [&](int kg) -> const char* {
+    const int32_t slot = kg == 0 ? slots[0] : kg == 1 ? slots[1] : kg == 2 ? slots[2] : slots[3];
+    const char* row = (slot >= 0 && slot < num_slots) ? kv_pool + (int64_t)slot * kRowBytes
+                                                      : reinterpret_cast<const char*>(g_zero_row);
+    return row + (s ^ (4 * (kg & 1) + (r >> 1))) * 16;
+  };
+  const char* own = row_of(gather_kg(j, 0));
 #pragma unroll
-  for (int L = 0; L < kGatherLoads; ++L) lds_dma16_nt(row + L * 128, tile + (gl.kg * 9 + L) * 1024);
+  for (int k = 0; k < kGatherLoads; ++k) {
+    const int kg = gather_kg(j, k), L = gather_line(j, k);
+    lds_dma16_nt((k < kOwnLoads ? own : row_of(kg)) + L * 128, tile + (kg * 9 + L) * 1024);
+  }
 }
 
 __device__ __forceinline__ LDS_AS char* lds_cast(char* p) { return (LDS_AS char*)(p); }
@@ -338,6 +369,48 @@ constexpr int kStageRow = kWaveDvBlocks * 32 * 2 + 16;
 constexpr int kStageBytes = 32 * kStageRow;
 static_assert(kSplitWaves * kStageBytes <= kOffXchg, "epilogue staging fits in the tile ring");
 
+// The refill of a tile slot (gather of tile u + 3 in phase X of iteration u)
+// races with no read of the slot's previous tile u. After the barrier that
+// opens phase X, the only reads of tile u are the odd waves' value reads:
+// wave w >= 4 reads line value_line(w) of every key group. The even waves
+// read their value lines before that barrier and both halves read tile u's
+// score operands (lines 0..8) one iteration earlier. Gather wave j (wave 4 + j)
+// issues its loads only after its own value reads are complete, so each
+// region it writes must be one that no other wave reads after the barrier;
+// and the four gather waves together must write every region exactly once.
+// Both are checked here over the same tables the gather and the value reads
+// use.
+__host__ __device__ constexpr bool read_after_phase_barrier(int wave, int line) {
+  return wave >= kSplitWaves / 2 && value_line(wave) == line;
+}
+__host__ __device__ constexpr bool gather_ownership_ok() {
+  int cover[kKeyGroups][kGatherLoads] = {};
+  for (int j = 0; j < kGatherWaves; ++j)
+    for (int k = 0; k < kGatherLoads; ++k) {
+      const int kg = gather_kg(j, k), L = gather_line(j, k);
+      if (kg < 0 || kg >= kKeyGroups || L < 0 || L >= kGatherLoads) return false;
+      ++cover[kg][L];
+      for (int w = 0; w < kSplitWaves; ++w)
+        if (w != kSplitWaves / 2 + j && read_after_phase_barrier(w, L)) return false;
+    }
+  for (int kg = 0; kg < kKeyGroups; ++kg)
+    for (int L = 0; L < kGatherLoads; ++L)
+      if (cover[kg][L] != 1) return false;
+  // every value chunk a wave reads lies in its value line
+  for (int w = 0; w < kSplitWaves; ++w)
+    for (int d = 0; d < kWaveDvBlocks; ++d)
+      for (int g = 0; g < 4; ++g)
+        for (int s = 0; s < 16; ++s)
+          if (value_chunk(w, d, g, s) / 8 != value_line(w)) return false;
+  // the slot ring: byte 4l of an entry holds key slot_copy_key(l); a gathering
+  // lane reads bytes 16r + 4kg for key 8kg + r (and lanes 32..63 repeat 0..31)
+  for (int r = 0; r < 8; ++r)
+    for (int kg = 0; kg < kKeyGroups; ++kg)
+      if (slot_copy_key(4 * r + kg) != 8 * kg + r || slot_copy_key(32 + 4 * r + kg) != 8 * kg + r) return false;
+  return true;
+}
+static_assert(gather_ownership_ok(), "a tile refill may overwrite a region another wave still reads");
+
 template <int V>
 struct IntC {
   static constexpr int value = V;
@@ -443,47 +516,54 @@ split_kernel(SplitArgs a) {
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int d = 0; d < 2; ++d)
-        tr_off[hf][d] = tile_offset(4 * (2 * wave + d) + 2 * (g & 1) + ((s & 3) >> 1), 8 * hh + 4 * hf + (s >> 2)) +
-                        (s & 1) * 8;
+        tr_off[hf][d] = tile_offset(value_chunk(wave, d, g, s), 8 * hh + 4 * hf + (s >> 2)) + (s & 1) * 8;
   };
   LDS_AS char* xchg = lds + kOffXchg + pair * kXchgBytes + lane * 16;   // + k * 1024
   LDS_AS char* pbuf = lds + kOffP + lane * 16;                          // + rb * kPBytes + t * 1024
   LDS_AS char* abuf = lds + kOffAlpha;
   LDS_AS char* fbuf = lds + kOffFlag;
 
-  // Gather bookkeeping (see gather_lane): the odd half (waves 4-7) issues all
-  // direct-to-LDS loads, nine per wave and tile; lane l always fetches the
-  // same key of a tile. The even half issues none inside the loop, so its
-  // LDS reads never wait on them.
-  // (The per-lane gather fields are re-derived from fresh_lane() at each use,
-  // so they do not occupy registers across the loop.)
-  auto glane = [&]() { return gather_lane(wave - 4, fresh_lane()); };
+  // Gather bookkeeping (see issue_tile_gather): the odd half (waves 4-7)
+  // issues all direct-to-LDS loads, nine per wave and tile; lane l always
+  // fetches key l/8 of each key group it covers. The even half issues none
+  // inside the loop, so its LDS reads never wait on them.
+  // (Per-lane values are re-derived from fresh_lane() at each use, so they
+  // do not occupy registers across the loop.)
   // Slot indices travel through LDS like the latent rows: wave 4 copies the
   // 32 kv_indices entries of tile v into ring entry v % 8 with one
-  // direct-to-LDS dword load (lanes 32-63 duplicate lanes 0-31), kSlotAhead
-  // tiles ahead, so that the vmcnt waits that cover the gathers cover them
-  // too. (A register load would make the compiler wait for it with a vmcnt
-  // that also drains the gathers issued after it.)
+  // direct-to-LDS dword load (in slot_copy_key order), kSlotAhead tiles ahead,
+  // so that the vmcnt waits that cover the gathers cover them too. (A
+  // register load would make the compiler wait for it with a vmcnt that also
+  // drains the gathers issued after it.)
   LDS_AS char* slot_ring = lds + kOffSlots;
-  auto tile_key_ok = [&](int v, int gkey) -> bool { return kstart + (int64_t)v * kUnit + gkey < kend; };
   auto load_slots_to_lds = [&](int v) {
     if (wave == 4) {
-      int64_t gpos = sbase + kstart + (int64_t)v * kUnit + (lane & 31);
+      int64_t gpos = sbase + kstart + (int64_t)v * kUnit + slot_copy_key(lane);
       gpos = gpos < a.total_kv ? gpos : a.total_kv - 1;
       gpos = gpos < 0 ? 0 : gpos;
       lds_dma4(a.kv_indices + gpos, slot_ring + (v % kSlotRing) * 256);
     }
   };
-  auto read_slot = [&](int v) -> int32_t {
-    const int gkey = glane().key;
-    const int32_t sl = *reinterpret_cast<LDS_AS const int32_t*>(slot_ring + (v % kSlotRing) * 256 + gkey * 4);
-    return tile_key_ok(v, gkey) ? sl : -1;
+  // Slots of this lane's key r = lane/8 in the four key groups of tile v
+  // (-1, the zero row, for keys past the chunk).
+  auto read_slots = [&](int v) -> i32x4g {
+    const int r = fresh_lane() >> 3;
+    i32x4g sl = *reinterpret_cast<LDS_AS const i32x4g*>(slot_ring + (v % kSlotRing) * 256 + r * 16);
+    const int64_t k0 = kstart + (int64_t)v * kUnit + r;
+#pragma unroll
+    for (int kg = 0; kg < kKeyGroups; ++kg) sl[kg] = k0 + 8 * kg < kend ? sl[kg] : -1;
+    return sl;
   };
-  auto load_slot = [&](int v) -> int32_t {
-    const int64_t pos = kstart + (int64_t)v * kUnit + glane().key;
-    return pos < kend ? a.kv_indices[sbase + pos] : -1;
+  auto load_slots = [&](int v) -> i32x4g {
+    const int64_t k0 = kstart + (int64_t)v * kUnit + (fresh_lane() >> 3);
+    i32x4g sl;
+#pragma unroll
+    for (int kg = 0; kg < kKeyGroups; ++kg) sl[kg] = k0 + 8 * kg < kend ? a.kv_indices[sbase + k0 + 8 * kg] : -1;
+    return sl;
   };
-  auto issue = [&](int32_t slot, LDS_AS char* tile) { issue_tile_gather(a.kv_pool, a.num_slots, slot, tile, glane()); };
+  auto issue = [&](i32x4g slots, LDS_AS char* tile) {
+    issue_tile_gather(a.kv_pool, a.num_slots, slots, tile, wave - kSplitWaves / 2, fresh_lane());
+  };
 
   // Online-softmax state of the pair's rows (log2 domain; kept by the even
   // half) and this wave's output accumulators O^T: [row block][value block].
@@ -695,9 +775,9 @@ split_kernel(SplitArgs a) {
     // half: queries and mask row.
     u32x4 qv[kHalfKSteps];
     if constexpr (PP == 1) {
-      const int32_t s0 = load_slot(0);
-      const int32_t s1 = load_slot(1);
-      const int32_t s2 = load_slot(2);
+      const i32x4g s0 = load_slots(0);
+      const i32x4g s1 = load_slots(1);
+      const i32x4g s2 = load_slots(2);
       load_q(qv);
       place_q(qv);
       issue(s0, lds);
@@ -765,10 +845,12 @@ split_kernel(SplitArgs a) {
         read_values(tile, vheld);
         if (more) write_xchg(sa);
         load_slots_to_lds(u + kSlotAhead);
-        const int32_t slot = read_slot(u + kGatherAhead);
-        // nobody reads tile u any more once this wave's value reads are done
+        const i32x4g slots = read_slots(u + kGatherAhead);
+        // The refill of tile u's slot with tile u + 3 writes, besides regions
+        // nobody reads after the phase barrier, only this wave's own value
+        // line (gather_ownership_ok), so it waits for this wave's reads alone.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        issue(slot, tile);
+        issue(slots, tile);
         // Tile u+2 has landed once no more than the loads issued after it are
         // outstanding: this phase's slot copy (wave 4) and its nine gather
         // loads. (The compiler does not track direct-to-LDS loads, so the wait
@@ -1006,21 +1088,33 @@ __global__ void __launch_bounds__(256) merge_few_kernel(const _Float16* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Debug gather: the split kernel's gather routine, copied back out in order.
+// Debug gather: the split kernel's slot copy and gather routines for one
+// tile per workgroup (wave 0 copies the 32 slot indices into LDS in
+// slot_copy_key order, each of the four waves reads its lanes' slots back and
+// issues its share of the gather), copied back out in position order.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(kGatherWaves * 64) debug_gather_kernel(const char* __restrict__ kv_pool,
                                                                          const int32_t* __restrict__ kv_indices,
                                                                          int64_t n, int64_t num_slots,
                                                                          u32x4* __restrict__ rows_out) {
-  __shared__ __attribute__((aligned(1024))) char smem[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[kTileBytes + 256];
   LDS_AS char* lds = lds_cast(smem);
+  LDS_AS char* ring = lds + kTileBytes;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const GatherLane gl = gather_lane(wave, lane);
   const int64_t ustart = (int64_t)blockIdx.x * kUnit;
-  const int64_t pos = ustart + gl.key;
-  const int32_t slot = pos < n ? kv_indices[pos] : -1;
-  issue_tile_gather(kv_pool, num_slots, slot, lds, gl);
+  if (wave == 0) {
+    int64_t pos = ustart + slot_copy_key(lane);
+    pos = pos < n ? pos : n - 1;
+    lds_dma4(kv_indices + pos, ring);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+  const int r = lane >> 3;
+  i32x4g sl = *reinterpret_cast<LDS_AS const i32x4g*>(ring + r * 16);
+#pragma unroll
+  for (int kg = 0; kg < kKeyGroups; ++kg) sl[kg] = ustart + 8 * kg + r < n ? sl[kg] : -1;
+  issue_tile_gather(kv_pool, num_slots, sl, lds, wave, lane);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int p = tid; p < kUnit * kChunks; p += kGatherWaves * 64) {
