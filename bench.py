@@ -1,18 +1,23 @@
 #!/usr/bin/env python3
 """Benchmark: MLA speculative-decoding verify attention on one MI355X.
 
-One step = one verify_attn() call (plan + split + merge kernels) over the
-long-context workload: 1 sequence, 64 heads, 16 verify positions in a causal
-chain, prefix 185,000, page_size 1 with shuffled kv_indices into a 512k-slot
-pool, bf16 N(0,1) latents, q = 0.5 N(0,1), scale 1/sqrt(192). Inputs are
-seeded and synthetic and are resident in HBM before timing starts.
+One step = one verify_attn() call (split + merge kernels) over the
+long-context workload by default: 1 sequence, 64 heads, 16 verify positions in
+a causal chain, prefix 185,000, page_size 1 with shuffled kv_indices into a
+512k-slot pool, bf16 N(0,1) latents, q = 0.5 N(0,1), scale 1/sqrt(192)
+(--config picks another workload). Inputs are seeded and synthetic and are
+resident in HBM before timing starts.
 
-Before each timed call a 1 GiB fill evicts the caches (the 256 MiB last-level
+Before each cold call a 1 GiB read evicts the caches (the 256 MiB last-level
 cache would otherwise hold most of the 213 MB KV working set); call and split
 kernel times come from HIP events on the call's stream. The JSON line reports
 us/call (lower is better), algorithmic HBM GB/s against 8 TB/s, the split
-kernel's MFMA roofline fraction, and the fp64 CPU oracle timed on a bounded
-sample of the same workload.
+kernel's roofline fraction (MFMA or HBM, whichever binds the workload), and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
+
+--summarize-trace CSV turns a rocprofv3 kernel trace of a bench run into the
+per-kernel averages of the timed calls alone (warmup calls dropped, cold and
+warm calls apart), for the profile summaries.
 """
 
 from __future__ import annotations
@@ -29,7 +34,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-METRIC = "verify-attn µs/call + achieved HBM GB/s (% of peak), 64 heads, 185k prefix"
+METRIC = "verify-attn µs/call + achieved HBM GB/s (% of peak), 64 heads, 185k prefix"   # the long185k line
 PEAK_HBM = 8.0e12            # MI355X HBM3E, bytes/s
 PEAK_MFMA_BF16 = 2.5e15      # MI355X dense bf16/fp16 MFMA, FLOP/s
 FLOP_PER_PAIR = 2 * (576 + 512)   # q.k over 576 dims + p*v over 512 dims, per visible (row, key)
@@ -48,6 +53,16 @@ WORKLOAD_TEXT = {
     "long185k_contig": "long185k over a defragmented cache: contiguous kv_indices (arange), 185016-slot pool",
     "long185k_h8_contig": "long185k_h8 over a defragmented cache: contiguous kv_indices (arange), 185016-slot pool",
 }
+
+
+def metric_for(name: str, w) -> str:
+    """The metric string of a bench line, naming the workload actually run (the 64-head,
+    185k-prefix workload keeps the headline metric's own wording)."""
+    if name == "long185k":
+        return METRIC
+    prefix = (f"{int(w.prefix_lens[0])} prefix" if w.B == 1 else
+              f"{w.B} sequences, prefixes {int(w.prefix_lens.min())}..{int(w.prefix_lens.max())}")
+    return f"verify-attn µs/call + achieved HBM GB/s (% of peak), {w.H} heads, {w.Q} verify positions, {prefix}"
 
 
 def algorithmic_bytes(w) -> int:
@@ -244,6 +259,52 @@ def bench_tree_accept(args, torch, va) -> int:
     return 0
 
 
+def summarize_trace(path: str, config: str, warmup: int, steps: int) -> str:
+    """Markdown summary of a rocprofv3 kernel-trace CSV of `bench.py --config config
+    --warmup W --steps K`: the split and merge kernels of the timed calls only. The run
+    makes W warmup calls, then K steps of four calls (cold call, cold split-kernel
+    timing, warm call, warm split-kernel timing); each call is one split and one merge
+    dispatch, in that order."""
+    import csv
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+    split = [r for r in rows if "split_kernel" in r["Kernel_Name"]]
+    merge = [r for r in rows if "merge" in r["Kernel_Name"] and "va" in r["Kernel_Name"]]
+    n = warmup + 4 * steps
+    if len(split) != n or len(merge) != n:
+        raise SystemExit(f"expected {n} split and merge dispatches, found {len(split)} and {len(merge)}")
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3  # noqa: E731
+    kinds = {"cold": (0, 1), "warm": (2, 3)}
+    w = None
+    out = [f"Timed calls only: the first {warmup} calls (warmup) are dropped; {steps} steps of four calls "
+           "remain (cold call, cold split-kernel timing, warm call, warm split-kernel timing).", "",
+           "| kernel | calls | kind | avg us | min us | max us |", "|---|---:|---|---:|---:|---:|"]
+    stats = {}
+    for kind, idx in kinds.items():
+        sel = [warmup + 4 * k + i for k in range(steps) for i in idx]
+        for name, lst in (("split_kernel", split), (merge[0]["Kernel_Name"].split("(")[0], merge)):
+            d = np.array([dur(lst[i]) for i in sel])
+            stats[(name, kind)] = d
+            short = "merge_few_kernel" if "few" in name else ("merge_kernel" if "merge" in name else name)
+            out.append(f"| {short} | {len(d)} | {kind} | {d.mean():.2f} | {d.min():.2f} | {d.max():.2f} |")
+        calls = np.array([(int(merge[i]["End_Timestamp"]) - int(split[i]["Start_Timestamp"])) / 1e3 for i in sel])
+        out.append(f"| whole call (split start to merge end) | {len(calls)} | {kind} | {calls.mean():.2f} | "
+                   f"{calls.min():.2f} | {calls.max():.2f} |")
+        stats[("call", kind)] = calls
+    from workloads import make_config
+    w = make_config(config)
+    flops = visible_pairs(w) * FLOP_PER_PAIR
+    split_bytes = int(w.total_kv) * 1152
+    cold = float(stats[("split_kernel", "cold")].mean())
+    if flops / PEAK_MFMA_BF16 >= split_bytes / PEAK_HBM:
+        a = flops / (cold * 1e-6) / 1e12
+        roof = f"MFMA-bound: {flops} FLOP per launch / {cold:.2f} us = {a:.1f} TFLOP/s, frac {a * 1e12 / PEAK_MFMA_BF16:.4f} of 2500 TFLOP/s"
+    else:
+        a = split_bytes / (cold * 1e-6) / 1e9
+        roof = f"HBM-bound: {split_bytes} B of KV rows per launch / {cold:.2f} us = {a:.1f} GB/s, frac {a * 1e9 / PEAK_HBM:.4f} of 8000 GB/s"
+    out += ["", f"Roofline of the split kernel from the cold average above: {roof}."]
+    return "\n".join(out)
+
+
 def copy_calibration(nbytes: int = 1 << 30, reps: int = 3) -> None:
     """A plain device copy of known size, for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE."""
     import torch
@@ -259,16 +320,23 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="long185k", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="skip the cache eviction between calls")
     ap.add_argument("--chunk", type=int, default=0, help="keys-per-chunk override (0 = automatic)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-trace", metavar="CSV", default=None,
+                    help="print the timed-call summary of a rocprofv3 kernel trace of a bench run made with "
+                         "the same --config, --warmup and --steps, and exit (no GPU needed)")
     ap.add_argument("--op", default="attn", choices=["attn", "defrag", "tree_accept"],
                     help="attn (default): the verify-attention call; defrag / tree_accept: the steps next "
                          "to it, each with its own metric line")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.config, args.warmup, args.steps))
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -299,16 +367,16 @@ def main() -> int:
     idx = torch.from_numpy(w.kv_indices).to(dev)
     pl = torch.from_numpy(w.prefix_lens).to(dev)
     tm = torch.from_numpy(w.tree_mask).to(dev)
-    va.set_chunk_override(args.chunk)
-    plan = va.query_plan(w.B, w.Q, w.H, w.total_kv)
-    ws = va.alloc_workspace(w.B, w.Q, w.H, w.total_kv, device=dev)
+    plan = va.query_plan(w.B, w.Q, w.H, w.total_kv, chunk_keys=args.chunk)
+    ws = va.alloc_workspace(w.B, w.Q, w.H, w.total_kv, device=dev, chunk_keys=args.chunk)
     out = torch.empty((w.B, w.Q, w.H, 512), dtype=torch.float32, device=dev)
     lse = torch.empty((w.B, w.Q, w.H), dtype=torch.float32, device=dev)
     flush = None if args.no_flush else Evictor(torch, dev)
     scale = float(w.scale)
 
-    def call():
-        va.verify_attn(q, kv, idx, pl, tm, scale, out=out, lse=lse, workspace=ws)
+    def call(split_events=None):
+        va.verify_attn(q, kv, idx, pl, tm, scale, out=out, lse=lse, workspace=ws, chunk_keys=args.chunk,
+                       split_events=split_events)
 
     print(f"[bench] plan {plan}; warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -335,14 +403,11 @@ def main() -> int:
             for j, cold in ((0, True), (4, False)):
                 if cold and do_flush:
                     flush()
-                va.set_split_events(e[j], None)
-                call()
+                call(split_events=(e[j], None))
                 e[j + 1].record()
                 if cold and do_flush:
                     flush()
-                va.set_split_events(e[j + 2], e[j + 3])
-                call()
-            va.set_split_events(None, None)
+                call(split_events=(e[j + 2], e[j + 3]))
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         t = lambda i: np.array([x[i].elapsed_time(x[i + 1]) for x in ev]) * 1e3  # noqa: E731
@@ -367,7 +432,7 @@ def main() -> int:
         roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM / 1e9,
                 "unit": "GB/s", "frac": round(gbps * 1e9 / PEAK_HBM, 4)}
     result = {
-        "metric": METRIC,
+        "metric": metric_for(args.config, w),
         "value": round(us, 2),
         "unit": "µs/call",
         "n_gpus": 1,

@@ -65,9 +65,11 @@ typedef enum {
 } va_status;
 
 /*
- * Bytes of device workspace verify_attn() needs for these sizes on the
- * current HIP device (the split plan depends on its compute-unit count).
- * Returns 0 if the sizes are invalid.
+ * Not on the pages: added because the caller owns all device memory. Bytes
+ * of device workspace verify_attn() needs for these sizes on the current HIP
+ * device (the split plan depends on its compute-unit count): the chunk
+ * offsets, and the per-chunk partial outputs and log-sum-exps that the merge
+ * folds. Returns 0 if the sizes are invalid.
  */
 size_t verify_attn_workspace_size(int B, int Q, int H, int64_t total_kv);
 
@@ -95,55 +97,21 @@ size_t verify_attn_workspace_size(int B, int Q, int H, int64_t total_kv);
  * Device-side preconditions that the host cannot check: the prefix_lens
  * sum must match total_kv (positions past total_kv are treated as absent),
  * inputs must be finite, and value elements must lie within the finite
- * fp16 range (|v| < 65504), since the probability-times-value product runs
- * in fp16 (see the design notes on precision).
+ * fp16 range (|v| < 65504): the probability-times-value product takes its
+ * operands in fp16 and each chunk's normalised partial output is kept in
+ * fp16, so a larger value becomes inf or NaN without an error. The absolute
+ * error grows with the values (fp16 rounding is relative to magnitude).
  */
 int verify_attn(const void* q, const void* kv_pool, const int32_t* kv_indices,
                 const int32_t* prefix_lens, const uint8_t* tree_mask, float scale,
                 float* out, float* lse, int B, int Q, int H, int64_t num_slots,
                 int64_t total_kv, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Thread-local description of the last error on this thread ("" if none). */
+/*
+ * Not on the pages: added because a C ABI carries no exceptions.
+ * Thread-local description of the last error on this thread ("" if none).
+ */
 const char* verify_attn_last_error(void);
-
-/*
- * Test hook: runs the split kernel's own gather routine (kv_indices -> 16-byte
- * direct-to-LDS loads -> LDS tile) for positions 0..n-1 and copies each tile
- * back out in position order, so the gather can be compared bit-exactly with
- * kv_pool[kv_indices[j]]. rows_out is bf16 [n][576], 16-byte aligned. Slots
- * outside [0, num_slots) produce zero rows, as in verify_attn().
- */
-int verify_attn_debug_gather(const void* kv_pool, const int32_t* kv_indices, int64_t n,
-                             int64_t num_slots, void* rows_out, void* stream);
-
-/*
- * The split plan verify_attn() would use for these sizes on the current
- * device: the shortest keys per chunk (the device may pick a longer length,
- * the shortest whose chunks fit in the chunk budget of the grid, from the
- * actual prefix lengths), the chunk capacity of the workspace, row tiles per
- * sequence (128 query-head rows each) and the split-kernel grid size. Any
- * output pointer may be NULL. Returns VA_OK or VA_EINVAL.
- */
-int verify_attn_query_plan(int B, int Q, int H, int64_t total_kv, int32_t* chunk_keys,
-                           int32_t* max_chunks, int32_t* row_tiles, int32_t* grid);
-
-/*
- * Profiling hook (thread-local): every later verify_attn() call on this
- * thread records start_event (if non-NULL) on its stream right before
- * launching the split kernel, its first launch, and stop_event (if non-NULL)
- * right after it. Both time the split kernel alone; start_event alone, with
- * an event the caller records after the call, times the whole call from its
- * first kernel. Events are hipEvent_t passed as void*, created and owned by
- * the caller. Passing NULL, NULL turns it off.
- */
-void verify_attn_set_split_events(void* start_event, void* stop_event);
-
-/*
- * Process-wide override of the keys per chunk (rounded up to a multiple of 32;
- * 0 restores the automatic choice). Meant for tuning sweeps; the workspace
- * size depends on it, so query the size again after changing it.
- */
-void verify_attn_set_chunk_override(int32_t chunk_keys);
 
 /*
  * KV-cache defragmentation (page "The Build That Unlocked 3-6x Decode

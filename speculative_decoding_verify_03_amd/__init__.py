@@ -25,13 +25,21 @@ EXPORTED = (
     "verify_attn",
     "verify_attn_workspace_size",
     "verify_attn_last_error",
-    "verify_attn_debug_gather",
-    "verify_attn_query_plan",
-    "verify_attn_set_chunk_override",
-    "verify_attn_set_split_events",
     "verify_attn_kv_defrag",
     "verify_attn_tree_accept",
+    # test and measurement interface (include/verify_attn_testing.h)
+    "verify_attn_ex",
+    "verify_attn_workspace_size_ex",
+    "verify_attn_query_plan",
+    "verify_attn_debug_gather",
 )
+
+
+class _TestOptions(ctypes.Structure):
+    """va_test_options of include/verify_attn_testing.h."""
+    _fields_ = [("chunk_keys", ctypes.c_int32), ("split_start_event", ctypes.c_void_p),
+                ("split_stop_event", ctypes.c_void_p)]
+
 
 _lib = None
 
@@ -62,15 +70,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.verify_attn_workspace_size.restype = sz
     lib.verify_attn_last_error.argtypes = []
     lib.verify_attn_last_error.restype = ctypes.c_char_p
+    lib.verify_attn_ex.argtypes = lib.verify_attn.argtypes + [ctypes.POINTER(_TestOptions)]
+    lib.verify_attn_ex.restype = i32
+    lib.verify_attn_workspace_size_ex.argtypes = [i32, i32, i32, i64, ctypes.c_int32]
+    lib.verify_attn_workspace_size_ex.restype = sz
     lib.verify_attn_debug_gather.argtypes = [vp, vp, i64, i64, vp, vp]
     lib.verify_attn_debug_gather.restype = i32
     p32 = ctypes.POINTER(ctypes.c_int32)
-    lib.verify_attn_query_plan.argtypes = [i32, i32, i32, i64, p32, p32, p32, p32]
+    lib.verify_attn_query_plan.argtypes = [i32, i32, i32, i64, ctypes.c_int32, p32, p32, p32, p32]
     lib.verify_attn_query_plan.restype = i32
-    lib.verify_attn_set_chunk_override.argtypes = [ctypes.c_int32]
-    lib.verify_attn_set_chunk_override.restype = None
-    lib.verify_attn_set_split_events.argtypes = [vp, vp]
-    lib.verify_attn_set_split_events.restype = None
     lib.verify_attn_kv_defrag.argtypes = [vp, vp, i64, i64, vp, i64, i64, vp, vp]
     lib.verify_attn_kv_defrag.restype = i32
     lib.verify_attn_tree_accept.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp]
@@ -95,44 +103,45 @@ def _stream_handle(stream) -> Optional[int]:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def workspace_size(B: int, Q: int, H: int, total_kv: int) -> int:
-    n = load_library().verify_attn_workspace_size(B, Q, H, total_kv)
+def workspace_size(B: int, Q: int, H: int, total_kv: int, chunk_keys: int = 0) -> int:
+    """Workspace bytes of a call (chunk_keys > 0: with that forced chunk length)."""
+    lib = load_library()
+    if chunk_keys:
+        n = lib.verify_attn_workspace_size_ex(B, Q, H, total_kv, int(chunk_keys))
+    else:
+        n = lib.verify_attn_workspace_size(B, Q, H, total_kv)
     if n == 0:
-        raise VerifyAttnError(VA_EINVAL, f"invalid sizes B={B} Q={Q} H={H} total_kv={total_kv}")
+        raise VerifyAttnError(VA_EINVAL, f"invalid sizes B={B} Q={Q} H={H} total_kv={total_kv} "
+                                         f"chunk_keys={chunk_keys}")
     return int(n)
 
 
-def query_plan(B: int, Q: int, H: int, total_kv: int) -> Dict[str, int]:
+def query_plan(B: int, Q: int, H: int, total_kv: int, chunk_keys: int = 0) -> Dict[str, int]:
     vals = [ctypes.c_int32() for _ in range(4)]
-    _check(load_library().verify_attn_query_plan(B, Q, H, total_kv, *[ctypes.byref(v) for v in vals]))
+    _check(load_library().verify_attn_query_plan(B, Q, H, total_kv, int(chunk_keys),
+                                                 *[ctypes.byref(v) for v in vals]))
     return dict(zip(("chunk_keys", "max_chunks", "row_tiles", "grid"), (v.value for v in vals)))
 
 
-def set_chunk_override(chunk_keys: int) -> None:
-    """Process-wide keys-per-chunk override for tuning sweeps (0 = automatic)."""
-    load_library().verify_attn_set_chunk_override(int(chunk_keys))
-
-
-def set_split_events(start_event=None, stop_event=None) -> None:
-    """Record these torch.cuda.Events right before / after the split kernel of later
-    calls (either may be None: not recorded)."""
-    h = lambda e: None if e is None else int(e.cuda_event)  # noqa: E731
-    load_library().verify_attn_set_split_events(h(start_event), h(stop_event))
-
-
-def alloc_workspace(B: int, Q: int, H: int, total_kv: int, device="cuda"):
+def alloc_workspace(B: int, Q: int, H: int, total_kv: int, device="cuda", chunk_keys: int = 0):
     import torch
-    return torch.empty(workspace_size(B, Q, H, total_kv), dtype=torch.uint8, device=device)
+    return torch.empty(workspace_size(B, Q, H, total_kv, chunk_keys), dtype=torch.uint8, device=device)
 
 
 def verify_attn(q, kv_pool, kv_indices, prefix_lens, tree_mask, scale: float,
-                out=None, lse=None, workspace=None, stream=None) -> Tuple[object, object]:
+                out=None, lse=None, workspace=None, stream=None, chunk_keys: int = 0,
+                split_events=None) -> Tuple[object, object]:
     """Verify attention over a paged MLA latent cache (see include/verify_attn.h).
 
     q: bf16 (or int16 bit patterns) [B, Q, H, 576]; kv_pool: bf16 [S, 576];
     kv_indices: int32 [total_kv]; prefix_lens: int32 [B]; tree_mask: uint8
     [B, Q, Q]; all CUDA tensors, contiguous. Returns (out fp32 [B, Q, H, 512],
     lse fp32 [B, Q, H]). Asynchronous on ``stream`` (default: current stream).
+
+    Test and measurement options (include/verify_attn_testing.h), per call:
+    ``chunk_keys`` > 0 forces the keys per chunk; ``split_events`` = (start,
+    stop) torch.cuda.Events (either may be None) recorded around the split
+    kernel. With neither, the plain ``verify_attn`` entry point is called.
     """
     import torch
     lib = load_library()
@@ -157,12 +166,17 @@ def verify_attn(q, kv_pool, kv_indices, prefix_lens, tree_mask, scale: float,
     if lse is None:
         lse = torch.empty((B, Q, H), dtype=torch.float32, device=q.device)
     if workspace is None:
-        workspace = alloc_workspace(B, Q, H, total_kv, device=q.device)
-    code = lib.verify_attn(_ptr(q), _ptr(kv_pool), _ptr(kv_indices), _ptr(prefix_lens),
-                           _ptr(tree_mask), float(scale), _ptr(out), _ptr(lse), B, Q, H,
-                           int(kv_pool.shape[0]), total_kv, _ptr(workspace),
-                           int(workspace.numel() * workspace.element_size()),
-                           _stream_handle(stream))
+        workspace = alloc_workspace(B, Q, H, total_kv, device=q.device, chunk_keys=chunk_keys)
+    args = (_ptr(q), _ptr(kv_pool), _ptr(kv_indices), _ptr(prefix_lens), _ptr(tree_mask), float(scale),
+            _ptr(out), _ptr(lse), B, Q, H, int(kv_pool.shape[0]), total_kv, _ptr(workspace),
+            int(workspace.numel() * workspace.element_size()), _stream_handle(stream))
+    if chunk_keys or split_events is not None:
+        ev0, ev1 = split_events if split_events is not None else (None, None)
+        h = lambda e: None if e is None else int(e.cuda_event)  # noqa: E731
+        opts = _TestOptions(int(chunk_keys), h(ev0), h(ev1))
+        code = lib.verify_attn_ex(*args, ctypes.byref(opts))
+    else:
+        code = lib.verify_attn(*args)
     _check(code)
     return out, lse
 

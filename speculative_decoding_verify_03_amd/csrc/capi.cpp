@@ -1,7 +1,9 @@
 // C-ABI shim of libverify_attn.so: argument validation, the split plan,
-// workspace carving and the three launches (plan, split, merge). The ABI is
-// declared in include/verify_attn.h. No entry point allocates, synchronises
-// or reads device memory on the host.
+// workspace carving and the two launches of a call (split kernel, then merge
+// kernel). The ABI is declared in include/verify_attn.h and, for tests and
+// measurement, include/verify_attn_testing.h. No entry point allocates,
+// synchronises or reads device memory on the host, and none keeps state
+// between calls other than a per-device cache of the compute-unit count.
 
 #include <hip/hip_runtime.h>
 
@@ -14,13 +16,11 @@
 
 #include "va_internal.hpp"
 #include "verify_attn.h"
+#include "verify_attn_testing.h"
 
 namespace {
 
 thread_local std::string g_last_error;
-thread_local hipEvent_t g_split_start = nullptr;
-thread_local hipEvent_t g_split_stop = nullptr;
-std::atomic<int32_t> g_chunk_override{0};
 std::atomic<int> g_cu_count[64];
 
 int fail(int code, const char* fmt, ...) {
@@ -65,15 +65,16 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // workgroup fills a compute unit (8 waves, ~159 KiB of LDS), so the batch
 // gets a budget of floor(CUs / row_tiles) chunks; the split kernel then picks
 // the shortest chunk length (at least total_kv / budget) whose chunks fit in
-// the budget.
-bool make_plan(int B, int Q, int H, int64_t total_kv, int ncu, va::Plan* p) {
+// the budget. A forced chunk length (chunk_keys > 0, tests and tuning only)
+// is used as is.
+bool make_plan(int B, int Q, int H, int64_t total_kv, int ncu, int32_t chunk_keys, va::Plan* p) {
   if (!dims_ok(B, Q, H, total_kv)) return false;
   const int64_t R = (int64_t)Q * H;
   p->row_tiles = (int32_t)((R + va::kRowsPerWG - 1) / va::kRowsPerWG);
   int64_t target = ncu / p->row_tiles;
   if (target < 1) target = 1;
   int64_t ideal = (total_kv + target - 1) / target;
-  const int32_t ov = g_chunk_override.load(std::memory_order_relaxed);
+  const int32_t ov = chunk_keys > 0 ? chunk_keys : 0;
   if (ov > 0) ideal = ov;
   if (ideal < va::kMinChunk && ov <= 0) ideal = va::kMinChunk;
   ideal = (ideal + va::kUnit - 1) / va::kUnit * va::kUnit;
@@ -103,34 +104,117 @@ bool make_plan(int B, int Q, int H, int64_t total_kv, int ncu, va::Plan* p) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// Host-side checks of a verify call's arguments other than the workspace;
+// fills the plan. Returns VA_OK or the status to report.
+int check_verify_args(const void* q, const void* kv_pool, const int32_t* kv_indices, const int32_t* prefix_lens,
+                      const uint8_t* tree_mask, float scale, const float* out, const float* lse, int B, int Q,
+                      int H, int64_t num_slots, int64_t total_kv, int32_t chunk_keys, va::Plan* p) {
+  if (!q || !kv_pool || !kv_indices || !prefix_lens || !tree_mask || !out || !lse)
+    return fail(VA_EINVAL, "null pointer argument");
+  if (!aligned(q, 16) || !aligned(kv_pool, 16) || !aligned(out, 16))
+    return fail(VA_EINVAL, "q, kv_pool and out must be 16-byte aligned");
+  if (!aligned(kv_indices, 4) || !aligned(prefix_lens, 4) || !aligned(lse, 4))
+    return fail(VA_EINVAL, "kv_indices, prefix_lens and lse must be 4-byte aligned");
+  if (!dims_ok(B, Q, H, total_kv))
+    return fail(VA_EINVAL, "bad sizes: B=%d Q=%d H=%d total_kv=%lld (need B>=1, 1<=Q<=%d, H>=1, "
+                "B*Q <= total_kv < 2^31)", B, Q, H, (long long)total_kv, VA_MAX_Q);
+  if (num_slots < 1 || num_slots > INT64_MAX / va::kRowBytes)
+    return fail(VA_EINVAL, "bad num_slots %lld", (long long)num_slots);
+  if (!std::isfinite(scale)) return fail(VA_EINVAL, "scale must be finite");
+  if (chunk_keys < 0) return fail(VA_EINVAL, "bad chunk_keys %d", chunk_keys);
+  if (!make_plan(B, Q, H, total_kv, cu_count(), chunk_keys, p)) return fail(VA_EINVAL, "sizes too large to plan");
+  return VA_OK;
+}
+
+// The two launches of a call, on a checked plan and a workspace of at least
+// p.bytes bytes (256-byte aligned). ev0 / ev1 (may be null) are recorded right
+// before and after the split kernel.
+int launch_verify(const void* q, const void* kv_pool, const int32_t* kv_indices, const int32_t* prefix_lens,
+                  const uint8_t* tree_mask, float scale, float* out, float* lse, int B, int Q, int H,
+                  int64_t num_slots, int64_t total_kv, const va::Plan& p, char* ws, hipStream_t st,
+                  hipEvent_t ev0, hipEvent_t ev1) {
+  auto* chunk_off = reinterpret_cast<int32_t*>(ws + p.off_chunk);
+  auto* part_lse = reinterpret_cast<float*>(ws + p.off_lse);
+  auto* part_o = reinterpret_cast<_Float16*>(ws + p.off_o);
+  hipError_t e = hipSuccess;
+
+  va::SplitArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.kv_pool = static_cast<const char*>(kv_pool);
+  a.kv_indices = kv_indices;
+  a.prefix_lens = prefix_lens;
+  a.tree_mask = tree_mask;
+  a.chunk_off = chunk_off;
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  a.num_slots = num_slots;
+  a.total_kv = total_kv;
+  a.B = B;
+  a.Q = Q;
+  a.H = H;
+  a.R = Q * H;
+  a.row_tiles = p.row_tiles;
+  a.ideal_keys = p.ideal_keys;
+  a.target = p.target;
+  a.max_chunks = p.max_chunks;
+  a.c_log2 = scale * 1.4426950408889634f;
+  if (ev0 != nullptr && (e = hipEventRecord(ev0, st)) != hipSuccess)
+    return fail(VA_EHIP, "event record: %s", hipGetErrorString(e));
+  e = va::launch_split(a, p.grid, st);
+  if (e != hipSuccess) return fail(VA_EHIP, "split launch: %s", hipGetErrorString(e));
+  if (ev1 != nullptr && (e = hipEventRecord(ev1, st)) != hipSuccess)
+    return fail(VA_EHIP, "event record: %s", hipGetErrorString(e));
+
+  e = va::launch_merge(part_o, part_lse, chunk_off, out, lse, B, Q * H, p.max_chunks, st);
+  if (e != hipSuccess) return fail(VA_EHIP, "merge launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int verify_with_workspace(const void* q, const void* kv_pool, const int32_t* kv_indices,
+                          const int32_t* prefix_lens, const uint8_t* tree_mask, float scale, float* out,
+                          float* lse, int B, int Q, int H, int64_t num_slots, int64_t total_kv, void* workspace,
+                          size_t workspace_bytes, void* stream, int32_t chunk_keys, hipEvent_t ev0,
+                          hipEvent_t ev1) {
+  try {
+    va::Plan p;
+    const int rc = check_verify_args(q, kv_pool, kv_indices, prefix_lens, tree_mask, scale, out, lse, B, Q, H,
+                                     num_slots, total_kv, chunk_keys, &p);
+    if (rc != VA_OK) return rc;
+    if (!workspace) return fail(VA_EINVAL, "null pointer argument");
+    if (!aligned(workspace, 256)) return fail(VA_EINVAL, "workspace must be 256-byte aligned");
+    if (workspace_bytes < p.bytes)
+      return fail(VA_ENOSPC, "workspace of %zu bytes < %zu needed", workspace_bytes, p.bytes);
+    return launch_verify(q, kv_pool, kv_indices, prefix_lens, tree_mask, scale, out, lse, B, Q, H, num_slots,
+                         total_kv, p, static_cast<char*>(workspace), static_cast<hipStream_t>(stream), ev0, ev1);
+  } catch (...) {
+    return fail(VA_EHIP, "unexpected C++ exception");
+  }
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t verify_attn_workspace_size(int B, int Q, int H, int64_t total_kv) {
+  return verify_attn_workspace_size_ex(B, Q, H, total_kv, 0);
+}
+
+size_t verify_attn_workspace_size_ex(int B, int Q, int H, int64_t total_kv, int32_t chunk_keys) {
   va::Plan p;
-  if (!make_plan(B, Q, H, total_kv, cu_count(), &p)) return 0;
+  if (chunk_keys < 0 || !make_plan(B, Q, H, total_kv, cu_count(), chunk_keys, &p)) return 0;
   return p.bytes;
 }
 
-int verify_attn_query_plan(int B, int Q, int H, int64_t total_kv, int32_t* chunk_keys,
+int verify_attn_query_plan(int B, int Q, int H, int64_t total_kv, int32_t chunk_keys_in, int32_t* chunk_keys,
                            int32_t* max_chunks, int32_t* row_tiles, int32_t* grid) {
   va::Plan p;
-  if (!make_plan(B, Q, H, total_kv, cu_count(), &p)) return fail(VA_EINVAL, "invalid sizes");
+  if (chunk_keys_in < 0 || !make_plan(B, Q, H, total_kv, cu_count(), chunk_keys_in, &p))
+    return fail(VA_EINVAL, "invalid sizes");
   if (chunk_keys) *chunk_keys = p.ideal_keys;
   if (max_chunks) *max_chunks = p.max_chunks;
   if (row_tiles) *row_tiles = p.row_tiles;
   if (grid) *grid = p.grid;
   return ok();
-}
-
-void verify_attn_set_split_events(void* start_event, void* stop_event) {
-  g_split_start = static_cast<hipEvent_t>(start_event);
-  g_split_stop = static_cast<hipEvent_t>(stop_event);
-}
-
-void verify_attn_set_chunk_override(int32_t chunk_keys) {
-  g_chunk_override.store(chunk_keys > 0 ? chunk_keys : 0, std::memory_order_relaxed);
 }
 
 const char* verify_attn_last_error(void) { return g_last_error.c_str(); }
@@ -139,65 +223,19 @@ int verify_attn(const void* q, const void* kv_pool, const int32_t* kv_indices,
                 const int32_t* prefix_lens, const uint8_t* tree_mask, float scale, float* out,
                 float* lse, int B, int Q, int H, int64_t num_slots, int64_t total_kv,
                 void* workspace, size_t workspace_bytes, void* stream) {
-  try {
-    if (!q || !kv_pool || !kv_indices || !prefix_lens || !tree_mask || !out || !lse || !workspace)
-      return fail(VA_EINVAL, "null pointer argument");
-    if (!aligned(q, 16) || !aligned(kv_pool, 16) || !aligned(out, 16))
-      return fail(VA_EINVAL, "q, kv_pool and out must be 16-byte aligned");
-    if (!aligned(kv_indices, 4) || !aligned(prefix_lens, 4) || !aligned(lse, 4))
-      return fail(VA_EINVAL, "kv_indices, prefix_lens and lse must be 4-byte aligned");
-    if (!aligned(workspace, 256)) return fail(VA_EINVAL, "workspace must be 256-byte aligned");
-    if (!dims_ok(B, Q, H, total_kv))
-      return fail(VA_EINVAL, "bad sizes: B=%d Q=%d H=%d total_kv=%lld (need B>=1, 1<=Q<=%d, H>=1, "
-                  "B*Q <= total_kv < 2^31)", B, Q, H, (long long)total_kv, VA_MAX_Q);
-    if (num_slots < 1 || num_slots > INT64_MAX / va::kRowBytes)
-      return fail(VA_EINVAL, "bad num_slots %lld", (long long)num_slots);
-    if (!std::isfinite(scale)) return fail(VA_EINVAL, "scale must be finite");
-    va::Plan p;
-    if (!make_plan(B, Q, H, total_kv, cu_count(), &p)) return fail(VA_EINVAL, "sizes too large to plan");
-    if (workspace_bytes < p.bytes)
-      return fail(VA_ENOSPC, "workspace of %zu bytes < %zu needed", workspace_bytes, p.bytes);
+  return verify_with_workspace(q, kv_pool, kv_indices, prefix_lens, tree_mask, scale, out, lse, B, Q, H,
+                               num_slots, total_kv, workspace, workspace_bytes, stream, 0, nullptr, nullptr);
+}
 
-    char* ws = static_cast<char*>(workspace);
-    auto* chunk_off = reinterpret_cast<int32_t*>(ws + p.off_chunk);
-    auto* part_lse = reinterpret_cast<float*>(ws + p.off_lse);
-    auto* part_o = reinterpret_cast<_Float16*>(ws + p.off_o);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = hipSuccess;
-
-    va::SplitArgs a;
-    a.q = static_cast<const uint16_t*>(q);
-    a.kv_pool = static_cast<const char*>(kv_pool);
-    a.kv_indices = kv_indices;
-    a.prefix_lens = prefix_lens;
-    a.tree_mask = tree_mask;
-    a.chunk_off = chunk_off;
-    a.part_o = part_o;
-    a.part_lse = part_lse;
-    a.num_slots = num_slots;
-    a.total_kv = total_kv;
-    a.B = B;
-    a.Q = Q;
-    a.H = H;
-    a.R = Q * H;
-    a.row_tiles = p.row_tiles;
-    a.ideal_keys = p.ideal_keys;
-    a.target = p.target;
-    a.max_chunks = p.max_chunks;
-    a.c_log2 = scale * 1.4426950408889634f;
-    if (g_split_start != nullptr && (e = hipEventRecord(g_split_start, st)) != hipSuccess)
-      return fail(VA_EHIP, "event record: %s", hipGetErrorString(e));
-    e = va::launch_split(a, p.grid, st);
-    if (e != hipSuccess) return fail(VA_EHIP, "split launch: %s", hipGetErrorString(e));
-    if (g_split_stop != nullptr && (e = hipEventRecord(g_split_stop, st)) != hipSuccess)
-      return fail(VA_EHIP, "event record: %s", hipGetErrorString(e));
-
-    e = va::launch_merge(part_o, part_lse, chunk_off, out, lse, B, Q * H, p.max_chunks, st);
-    if (e != hipSuccess) return fail(VA_EHIP, "merge launch: %s", hipGetErrorString(e));
-    return ok();
-  } catch (...) {
-    return fail(VA_EHIP, "unexpected C++ exception");
-  }
+int verify_attn_ex(const void* q, const void* kv_pool, const int32_t* kv_indices, const int32_t* prefix_lens,
+                   const uint8_t* tree_mask, float scale, float* out, float* lse, int B, int Q, int H,
+                   int64_t num_slots, int64_t total_kv, void* workspace, size_t workspace_bytes, void* stream,
+                   const va_test_options* opts) {
+  const int32_t ck = opts ? opts->chunk_keys : 0;
+  hipEvent_t e0 = opts ? static_cast<hipEvent_t>(opts->split_start_event) : nullptr;
+  hipEvent_t e1 = opts ? static_cast<hipEvent_t>(opts->split_stop_event) : nullptr;
+  return verify_with_workspace(q, kv_pool, kv_indices, prefix_lens, tree_mask, scale, out, lse, B, Q, H,
+                               num_slots, total_kv, workspace, workspace_bytes, stream, ck, e0, e1);
 }
 
 int verify_attn_debug_gather(const void* kv_pool, const int32_t* kv_indices, int64_t n,

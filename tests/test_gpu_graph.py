@@ -34,7 +34,6 @@ def _eager(torch, va, d, w, ws):
 
 def test_graph_replay_is_bitwise_eager_and_follows_new_lengths():
     torch, va = require_gpu()
-    va.set_chunk_override(0)
     # two sequences; the second input set moves 700 positions from the first
     # sequence's prefix to the second's, keeping total_kv (the capture key)
     w1 = make_workload("graph1", [310], B=2, Q=8, H=16, prefix_lens=[3000, 1200], mask="tree",
@@ -87,7 +86,6 @@ def test_graph_replay_time_small_call():
     """Launch overhead of a small call, eager against graph replay (reported), and the
     replayed result equals a later eager call bit for bit."""
     torch, va = require_gpu()
-    va.set_chunk_override(0)
     w = make_workload("graph_small", [312], B=1, Q=4, H=8, prefix_lens=[256], mask="chain", num_slots=1024)
     d = upload(w)
     ws = va.alloc_workspace(w.B, w.Q, w.H, w.total_kv, device="cuda")

@@ -1,9 +1,8 @@
 """GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
 
-Every comparison uses the same seeded inputs on both sides. Small workloads are
-compared element by element in full; the full-size workloads (launched with the
-same plan the benchmark uses) are compared on a sample of heads that the oracle
-computes exactly.
+Every comparison uses the same seeded inputs on both sides, element by element
+over the whole output, at every size: the full-size workloads run with the
+same plan the benchmark uses.
 """
 
 from __future__ import annotations
@@ -21,7 +20,6 @@ pytestmark = pytest.mark.gpu
 @pytest.fixture(scope="module")
 def env():
     torch, va = require_gpu()
-    va.set_chunk_override(0)
     return torch, va
 
 
@@ -48,14 +46,10 @@ def test_config_full_oracle(env, name):
     _check(env, make_config(name))
 
 
-@pytest.mark.parametrize("name,heads", [
-    ("long185k", [0, 21, 42, 63]),
-    ("batch8", [5, 38]),
-    ("long185k_h8", None),
-])
-def test_config_full_size_sampled(env, name, heads):
-    print(f"[parity] start {name} heads={heads}", flush=True)
-    _check(env, make_config(name), heads=heads)
+@pytest.mark.parametrize("name", ["long185k", "batch8", "long185k_h8"])
+def test_config_full_size_whole_output(env, name):
+    print(f"[parity] start {name} (all heads)", flush=True)
+    _check(env, make_config(name))
 
 
 EDGE_CASES = {
@@ -93,11 +87,7 @@ def test_many_small_chunks_cross_the_tail(env):
     # one, two, three and four tiles per chunk: the pipeline's prologue and
     # drain at every depth of the tile ring
     for chunk in (32, 64, 96, 128):
-        va.set_chunk_override(chunk)
-        try:
-            _check(env, w, label=f"chunk{chunk}")
-        finally:
-            va.set_chunk_override(0)
+        _check(env, w, label=f"chunk{chunk}", chunk_keys=chunk)
 
 
 def test_out_of_range_slots_read_as_zero_rows(env):
@@ -189,11 +179,7 @@ def test_late_max_growth_rescales_some_rows(env):
     qrow2 = w.q[0, 3, 30].astype(np.uint32) << 16         # another row grows in a different chunk
     w.kv_pool[w.kv_indices[700]] = bf16_from_f32(qrow2.view(np.float32) * np.float32(0.2))
     for chunk in (0, 1024):
-        va.set_chunk_override(chunk)
-        try:
-            _check(env, w, label=f"growth_chunk{chunk}")
-        finally:
-            va.set_chunk_override(0)
+        _check(env, w, label=f"growth_chunk{chunk}", chunk_keys=chunk)
 
 
 def _sweep_cases(n=24, seed=911):
@@ -222,11 +208,7 @@ def test_random_shape_sweep(env, case):
     w = make_workload(f"sweep{i}", [912, i], B=B, Q=Q, H=H, prefix_lens=prefix, mask=mask,
                       num_slots=sum(prefix) + B * Q + 64)
     print(f"[parity] sweep{i}: B={B} Q={Q} H={H} prefix={prefix} mask={mask} chunk={chunk}", flush=True)
-    va.set_chunk_override(chunk)
-    try:
-        _check(env, w, label=f"sweep{i}")
-    finally:
-        va.set_chunk_override(0)
+    _check(env, w, label=f"sweep{i}", chunk_keys=chunk)
 
 
 def _plan_model(w, plan, ncu):
