@@ -7,8 +7,9 @@ fp64 numpy (or pure Python for the brute force) and shares no code with the
 GPU implementation.
 
 Parity status: every function here is pinned by the CPU test suite against
-closed forms, invariants, a pure-Python brute force and torch's
-scaled_dot_product_attention in fp64; none is "parity unpinned".
+closed forms, invariants, a pure-Python brute force, independent rounding
+routines (Python's own binary16 packing, torch's bfloat16 conversion) and
+torch's scaled_dot_product_attention in fp64; none is "parity unpinned".
 """
 
 from .attention import (  # noqa: F401
@@ -24,6 +25,8 @@ from .attention import (  # noqa: F401
     lse_merge,
     split_merge_attention,
     online_softmax_attention,
+    chunked_attention_model,
+    round_to,
     brute_force,
 )
 from .kvcache import defrag  # noqa: F401

@@ -26,15 +26,20 @@ slots are the last Q entries of each sequence's ``kv_indices`` slice in query
 order; the tree mask includes the diagonal (a query sees its own tail key);
 the scale multiplies the fp64 dot product and is never folded into q.
 
-Besides the plain definition (``verify_attention``) this module carries two
+Besides the plain definition (``verify_attention``) this module carries
 restatements of the pages' flash-decode method, used only to pin the oracle
 and to model the kernel's rounding: a KV split with a log-sum-exp merge
 (``split_merge_attention``; the flash-decode KV split with its NSPLIT
 parameter, page "The Build That Unlocked 3-6x Decode Speedup", section "The
 Context: A Custom Kernel for an Unsupported Architecture", and page "The Build
 Script Edit: How a Single Line of Infrastructure Unlocked Custom CUDA Kernels
-on sm_120", section "Context: The Long Road to a Custom sm_120 Kernel") and
-online softmax over KV tiles (``online_softmax_attention``; same sections).
+on sm_120", section "Context: The Long Road to a Custom sm_120 Kernel"),
+online softmax over KV tiles (``online_softmax_attention``; same sections),
+and both together with a rounding model of where a kernel keeps which
+precision (``chunked_attention_model``, with ``round_to``; the pages stress
+the bf16 precision of their paged kernel, page "The Build That Bridged Design
+and Deployment: Compiling the Custom sm_120 Verify Kernel", section "What
+This Build Achieves: The paged+bf16 Kernel").
 """
 
 from __future__ import annotations
@@ -203,37 +208,117 @@ def split_merge_attention(q, kv_pool, kv_indices, prefix_lens, tree_mask, scale,
     return out, lse
 
 
-def _round_to(x: np.ndarray, kind: Optional[str]) -> np.ndarray:
-    """Round fp64 values to a storage type (used only by the precision model)."""
+def round_to(x: np.ndarray, kind: Optional[str]) -> np.ndarray:
+    """Round fp64 values to a storage type and back (the precision model only).
+
+    * None / "f64": unchanged.
+    * "f32": IEEE binary32, round to nearest, ties to even.
+    * "f16": IEEE binary16, round to nearest, ties to even, directly from the
+      fp64 value; gradual underflow to subnormals, overflow to +-inf.
+    * "bf16": first rounded to binary32 (the precision of the values a kernel
+      computes in fp32), then to bfloat16 (the upper half of a binary32),
+      round to nearest, ties to even; NaN stays NaN.
+    """
     if kind is None or kind == "f64":
         return x
+    x = np.asarray(x, dtype=np.float64)
     if kind == "f32":
         return x.astype(np.float32).astype(np.float64)
     if kind == "f16":
         return x.astype(np.float16).astype(np.float64)
     if kind == "bf16":
-        f = x.astype(np.float32)
+        f = np.ascontiguousarray(x.astype(np.float32))
         u = f.view(np.uint32)
         bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
         r = ((u + bias) >> np.uint32(16)) << np.uint32(16)
+        # a NaN whose payload sits in the low half would otherwise carry into
+        # the exponent's all-ones pattern and read as infinity
+        r = np.where(np.isnan(f), np.uint32(0x7FC00000), r).astype(np.uint32)
         return r.view(np.float32).astype(np.float64)
     raise ValueError(kind)
+
+
+def _online_rows(rows: np.ndarray, K: np.ndarray, vis: np.ndarray, scale: float, tile: int,
+                 p_round: Optional[str], v_round: Optional[str],
+                 score_round: Optional[str]) -> Tuple[np.ndarray, np.ndarray]:
+    """Online softmax of score rows over the keys K (the flash-decode inner loop).
+
+    rows [R, 576] fp64 queries, K [N, 576] fp64 latents (values = K[:, :512]),
+    vis [R, N] bool. Per row: a running max m, a running normaliser l and an
+    unnormalised accumulator o. For each tile of keys: m' = max(m, max s),
+    alpha = exp(m - m'), p = exp(s - m'), l = alpha l + sum p,
+    o = alpha o + round(p) round(V). Returns out = o / l and lse = m + log l
+    (a row that saw nothing: 0 and -inf). The p in l is not rounded: only the
+    value product's operands are.
+    """
+    R, N = rows.shape[0], K.shape[0]
+    V = round_to(K[:, :VALUE], v_round)
+    m = np.full(R, -np.inf)
+    l = np.zeros(R)
+    o = np.zeros((R, VALUE))
+    for lo in range(0, N, tile):
+        hi = min(N, lo + tile)
+        s = round_to(scale * (rows @ K[lo:hi].T), score_round)
+        s = np.where(vis[:, lo:hi], s, -np.inf)
+        m_new = np.maximum(m, s.max(axis=1))
+        live = np.isfinite(m_new)
+        ref = np.where(live, m_new, 0.0)
+        alpha = np.where(live, np.exp(np.where(np.isfinite(m), m, -np.inf) - ref), 1.0)
+        p = np.exp(s - ref[:, None])
+        l = alpha * l + p.sum(axis=1)
+        o = alpha[:, None] * o + round_to(p, p_round) @ V[lo:hi]
+        m = m_new
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ob = o / l[:, None]
+        lb = m + np.log(l)
+    empty = l == 0
+    ob[empty] = 0.0
+    lb[empty] = -np.inf
+    return ob, lb
 
 
 def online_softmax_attention(q, kv_pool, kv_indices, prefix_lens, tree_mask, scale,
                              tile: int = 32, p_round: Optional[str] = None,
                              v_round: Optional[str] = None,
                              score_round: Optional[str] = None) -> Tuple[np.ndarray, np.ndarray]:
-    """Online softmax over KV tiles (the flash-decode inner loop), one pass.
+    """Online softmax over KV tiles of ``tile`` keys, one pass per sequence
+    (see ``_online_rows``). ``p_round`` / ``v_round`` / ``score_round``
+    optionally round p, V or the scores to a storage type (``round_to``)
+    before use; that models where a kernel keeps which precision and is not
+    part of the definition."""
+    B, Q, H, _ = q.shape
+    scale = float(np.float32(scale))
+    off = sequence_offsets(prefix_lens, Q)
+    out = np.zeros((B, Q, H, VALUE))
+    lse = np.zeros((B, Q, H))
+    for b in range(B):
+        P = int(prefix_lens[b])
+        N = P + Q
+        K = gather_latents(kv_pool, kv_indices, int(off[b]), N)
+        vis = np.repeat(visibility(P, tree_mask[b]), H, axis=0)
+        rows = decode_bf16(q[b]).reshape(Q * H, LATENT)
+        ob, lb = _online_rows(rows, K, vis, scale, tile, p_round, v_round, score_round)
+        out[b] = ob.reshape(Q, H, VALUE)
+        lse[b] = lb.reshape(Q, H)
+    return out, lse
 
-    Per row: keep a running max m, a running normaliser l and an unnormalised
-    accumulator o. For each tile: m' = max(m, max s), alpha = exp(m - m'),
-    p = exp(s - m'), l = alpha l + sum p, o = alpha o + p V. At the end
-    out = o / l and lse = m + log l.
 
-    ``p_round`` / ``v_round`` / ``score_round`` optionally round p, V or the
-    scores to a storage type before use; that models where a kernel keeps
-    which precision and is not part of the definition.
+def chunked_attention_model(q, kv_pool, kv_indices, prefix_lens, tree_mask, scale, chunk: int,
+                            tile: int = 32, p_round: Optional[str] = "f16",
+                            v_round: Optional[str] = "f16",
+                            partial_round: Optional[str] = "f16") -> Tuple[np.ndarray, np.ndarray]:
+    """The pages' flash-decode method with a precision model: each sequence's
+    positions are cut into chunks of ``chunk`` keys (the last one shorter);
+    each chunk runs the online softmax over tiles of ``tile`` keys with p and V
+    rounded as given, leaves its normalised partial output rounded to
+    ``partial_round`` and its lse in fp64; the partials are merged by
+    log-sum-exp (``lse_merge``) in fp64.
+
+    With every rounding off this equals ``verify_attention`` up to fp64
+    rounding (the split-merge invariant). With the defaults it models the
+    precision the GPU kernel keeps (fp16 probabilities and values in the value
+    product, fp16 chunk partials), so that the error it predicts against the
+    exact result can be compared with the GPU's.
     """
     B, Q, H, _ = q.shape
     scale = float(np.float32(scale))
@@ -244,33 +329,17 @@ def online_softmax_attention(q, kv_pool, kv_indices, prefix_lens, tree_mask, sca
         P = int(prefix_lens[b])
         N = P + Q
         K = gather_latents(kv_pool, kv_indices, int(off[b]), N)
-        V = _round_to(K[:, :VALUE], v_round)
         vis = np.repeat(visibility(P, tree_mask[b]), H, axis=0)
         rows = decode_bf16(q[b]).reshape(Q * H, LATENT)
-        R = rows.shape[0]
-        m = np.full(R, -np.inf)
-        l = np.zeros(R)
-        o = np.zeros((R, VALUE))
-        for lo in range(0, N, tile):
-            hi = min(N, lo + tile)
-            s = _round_to(scale * (rows @ K[lo:hi].T), score_round)
-            s = np.where(vis[:, lo:hi], s, -np.inf)
-            m_new = np.maximum(m, s.max(axis=1))
-            live = np.isfinite(m_new)
-            ref = np.where(live, m_new, 0.0)
-            alpha = np.where(live, np.exp(np.where(np.isfinite(m), m, -np.inf) - ref), 1.0)
-            p = np.exp(s - ref[:, None])
-            l = alpha * l + p.sum(axis=1)
-            o = alpha[:, None] * o + _round_to(p, p_round) @ V[lo:hi]
-            m = m_new
-        with np.errstate(divide="ignore", invalid="ignore"):
-            ob = o / l[:, None]
-            lb = m + np.log(l)
-        empty = l == 0
-        ob[empty] = 0.0
-        lb[empty] = -np.inf
-        out[b] = ob.reshape(Q, H, VALUE)
-        lse[b] = lb.reshape(Q, H)
+        po, pl = [], []
+        for lo in range(0, N, chunk):
+            hi = min(N, lo + chunk)
+            o, l = _online_rows(rows, K[lo:hi], vis[:, lo:hi], scale, tile, p_round, v_round, None)
+            po.append(round_to(o, partial_round))
+            pl.append(l)
+        o, l = lse_merge(po, pl)
+        out[b] = o.reshape(Q, H, VALUE)
+        lse[b] = l.reshape(Q, H)
     return out, lse
 
 
