@@ -17,6 +17,9 @@ reading of greedy speculative decoding over a draft tree, taken here:
 * starting at the root, step to a child c of the current node whose draft
   token equals the target's choice at the current node, as long as one
   exists; when several children match, the one with the smallest index;
+* only a child with a larger index than the current node counts (every
+  well-formed tree has parents[i] < i, so this changes nothing there; on a
+  malformed parent array it keeps the walk finite, at most Q - 1 steps);
 * the result is the accepted path (root first), its length in draft tokens
   (path nodes minus the root), and the bonus token: the target's choice at
   the last accepted node.
@@ -40,7 +43,7 @@ def tree_accept(parents: np.ndarray, draft: np.ndarray, target: np.ndarray) -> T
     while True:
         nxt = None
         for c in range(q):                      # smallest matching child first
-            if c != 0 and parents[c] == cur and draft[c] == target[cur]:
+            if c > cur and parents[c] == cur and draft[c] == target[cur]:
                 nxt = c
                 break
         if nxt is None:

@@ -92,6 +92,11 @@ def _tree_pins(fn):
     assert fn(np.array([-1, 0, 1]), np.array([0, 1, 2]), np.array([5, 6, 7])) == (0, [0], 5)
     # two matching siblings: the smaller index wins
     assert fn(np.array([-1, 0, 0]), np.array([0, 3, 3]), np.array([3, 8, 9]))[1] == [0, 1]
+    # malformed parent arrays: only a child with a larger index than the current
+    # node counts (node 1 names the later node 2 as its parent and is skipped;
+    # a node that is its own parent is never a child of anything else)
+    assert fn(np.array([-1, 2, 0]), np.array([0, 5, 3]), np.array([3, 9, 5])) == (1, [0, 2], 5)
+    assert fn(np.array([-1, 1, 0, 2]), np.array([0, 4, 4, 6]), np.array([4, 4, 6, 1])) == (2, [0, 2, 3], 1)
     # chains: the accepted length is the length of the leading run of matches
     par, dr, tg = make_tree_accept_case(41, 16, 12, vocab=4, p_follow=0.8, chain=True)
     for b in range(16):
@@ -122,6 +127,18 @@ def test_tree_accept_batch_matches_single():
     for b in range(5):
         nb, path, tok = oracle.tree_accept(par[b], dr[b], tg[b])
         assert n[b] == nb and bonus[b] == tok and list(acc[b, :nb + 1]) == path and np.all(acc[b, nb + 1:] == -1)
+
+
+def _tree_any_index_child(parents, draft, target):
+    """Steps to a matching child whatever its index (no cycle in the pins' trees)."""
+    parents, draft, target = list(parents), list(draft), list(target)
+    q, cur, path = len(parents), 0, [0]
+    while True:
+        m = [c for c in range(1, q) if parents[c] == cur and draft[c] == target[cur] and c not in path]
+        if not m:
+            return len(path) - 1, path, target[cur]
+        cur = m[0]
+        path.append(cur)
 
 
 def _tree_largest_child(parents, draft, target):
@@ -157,7 +174,7 @@ def _tree_matches_own_token(parents, draft, target):
 
 
 @pytest.mark.parametrize("mutant", [_tree_largest_child, _tree_bonus_from_parent, _tree_counts_root,
-                                    _tree_matches_own_token])
+                                    _tree_matches_own_token, _tree_any_index_child])
 def test_tree_pins_catch_planted_mistakes(mutant):
     with pytest.raises(AssertionError):
         _tree_pins(mutant)
