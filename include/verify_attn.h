@@ -108,6 +108,25 @@ int verify_attn(const void* q, const void* kv_pool, const int32_t* kv_indices,
                 int64_t total_kv, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * computation as verify_attn(), with the same arguments except the
+ * workspace. It uses a fixed device scratch of VA_NOALLOC_SCRATCH_BYTES that
+ * the library holds on each device it runs on until the process ends, and
+ * calls no allocating routine. Sizes whose workspace
+ * (verify_attn_workspace_size) exceeds that scratch are rejected with
+ * VA_ENOSPC before anything is enqueued. Every call on a device shares that
+ * device's scratch: calls that may overlap on one device (different streams,
+ * different threads) race and must be ordered by the caller. Results equal
+ * verify_attn()'s bit for bit.
+ */
+#define VA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int verify_attn_noalloc(const void* q, const void* kv_pool, const int32_t* kv_indices,
+                        const int32_t* prefix_lens, const uint8_t* tree_mask, float scale,
+                        float* out, float* lse, int B, int Q, int H, int64_t num_slots,
+                        int64_t total_kv, void* stream);
+
+/*
  * Not on the pages: added because a C ABI carries no exceptions.
  * Thread-local description of the last error on this thread ("" if none).
  */

@@ -27,6 +27,7 @@ EXPORTED = (
     "verify_attn_last_error",
     "verify_attn_kv_defrag",
     "verify_attn_tree_accept",
+    "verify_attn_noalloc",
     # test and measurement interface (include/verify_attn_testing.h)
     "verify_attn_ex",
     "verify_attn_workspace_size_ex",
@@ -70,6 +71,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.verify_attn_workspace_size.restype = sz
     lib.verify_attn_last_error.argtypes = []
     lib.verify_attn_last_error.restype = ctypes.c_char_p
+    lib.verify_attn_noalloc.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, i32, i32, i32, i64, i64, vp]
+    lib.verify_attn_noalloc.restype = i32
     lib.verify_attn_ex.argtypes = lib.verify_attn.argtypes + [ctypes.POINTER(_TestOptions)]
     lib.verify_attn_ex.restype = i32
     lib.verify_attn_workspace_size_ex.argtypes = [i32, i32, i32, i64, ctypes.c_int32]
@@ -178,6 +181,34 @@ def verify_attn(q, kv_pool, kv_indices, prefix_lens, tree_mask, scale: float,
     else:
         code = lib.verify_attn(*args)
     _check(code)
+    return out, lse
+
+
+def verify_attn_noalloc(q, kv_pool, kv_indices, prefix_lens, tree_mask, scale: float, out, lse,
+                        stream=None) -> Tuple[object, object]:
+    """verify_attn through the allocation-free entry point: the library's fixed device
+    scratch replaces the workspace, and the caller passes preallocated ``out`` (fp32
+    [B, Q, H, 512]) and ``lse`` (fp32 [B, Q, H]). Calls that overlap on one device race."""
+    import torch
+    B, Q, H, D = q.shape
+    for name, t in (("q", q), ("kv_pool", kv_pool), ("kv_indices", kv_indices), ("prefix_lens", prefix_lens),
+                    ("tree_mask", tree_mask), ("out", out), ("lse", lse)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous CUDA tensor")
+    if D != LATENT_DIM or kv_pool.shape[-1] != LATENT_DIM or q.element_size() != 2 or kv_pool.element_size() != 2:
+        raise ValueError("q and kv_pool must be 16-bit [.., 576]")
+    if kv_indices.dtype != torch.int32 or prefix_lens.dtype != torch.int32 or tree_mask.dtype != torch.uint8:
+        raise ValueError("kv_indices and prefix_lens must be int32, tree_mask uint8")
+    if tuple(tree_mask.shape) != (B, Q, Q) or tuple(prefix_lens.shape) != (B,):
+        raise ValueError("tree_mask must be [B, Q, Q] and prefix_lens [B]")
+    if out.dtype != torch.float32 or tuple(out.shape) != (B, Q, H, VALUE_DIM):
+        raise ValueError("out must be fp32 [B, Q, H, 512]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Q, H):
+        raise ValueError("lse must be fp32 [B, Q, H]")
+    _check(load_library().verify_attn_noalloc(_ptr(q), _ptr(kv_pool), _ptr(kv_indices), _ptr(prefix_lens),
+                                              _ptr(tree_mask), float(scale), _ptr(out), _ptr(lse), B, Q, H,
+                                              int(kv_pool.shape[0]), int(kv_indices.numel()),
+                                              _stream_handle(stream)))
     return out, lse
 
 

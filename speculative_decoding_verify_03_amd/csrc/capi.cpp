@@ -18,6 +18,8 @@
 #include "verify_attn.h"
 #include "verify_attn_testing.h"
 
+static_assert(VA_NOALLOC_SCRATCH_BYTES == va::kNoAllocScratchBytes, "scratch size in the header");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -225,6 +227,27 @@ int verify_attn(const void* q, const void* kv_pool, const int32_t* kv_indices,
                 void* workspace, size_t workspace_bytes, void* stream) {
   return verify_with_workspace(q, kv_pool, kv_indices, prefix_lens, tree_mask, scale, out, lse, B, Q, H,
                                num_slots, total_kv, workspace, workspace_bytes, stream, 0, nullptr, nullptr);
+}
+
+int verify_attn_noalloc(const void* q, const void* kv_pool, const int32_t* kv_indices,
+                        const int32_t* prefix_lens, const uint8_t* tree_mask, float scale, float* out,
+                        float* lse, int B, int Q, int H, int64_t num_slots, int64_t total_kv, void* stream) {
+  try {
+    va::Plan p;
+    const int rc = check_verify_args(q, kv_pool, kv_indices, prefix_lens, tree_mask, scale, out, lse, B, Q, H,
+                                     num_slots, total_kv, 0, &p);
+    if (rc != VA_OK) return rc;
+    if (p.bytes > va::kNoAllocScratchBytes)
+      return fail(VA_ENOSPC, "these sizes need %zu bytes of scratch; the allocation-free entry point has a "
+                  "fixed %zu (use verify_attn with a workspace)", p.bytes, va::kNoAllocScratchBytes);
+    void* ws = nullptr;
+    const hipError_t e = va::noalloc_scratch(&ws);
+    if (e != hipSuccess) return fail(VA_EHIP, "scratch lookup: %s", hipGetErrorString(e));
+    return launch_verify(q, kv_pool, kv_indices, prefix_lens, tree_mask, scale, out, lse, B, Q, H, num_slots,
+                         total_kv, p, static_cast<char*>(ws), static_cast<hipStream_t>(stream), nullptr, nullptr);
+  } catch (...) {
+    return fail(VA_EHIP, "unexpected C++ exception");
+  }
 }
 
 int verify_attn_ex(const void* q, const void* kv_pool, const int32_t* kv_indices, const int32_t* prefix_lens,

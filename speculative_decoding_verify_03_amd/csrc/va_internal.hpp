@@ -49,6 +49,10 @@ struct SplitArgs {
 };
 
 hipError_t launch_split(const SplitArgs& a, int grid, hipStream_t stream);
+// Size of the allocation-free entry point's fixed device scratch, and its
+// device address on the current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(void** ptr);
 // The merge: the one-wave-per-row form when the partial buffers hold at most
 // kMergeFewPerSeq chunks per sequence on average, else the chunk-lane form.
 constexpr int kMergeFewPerSeq = 16;

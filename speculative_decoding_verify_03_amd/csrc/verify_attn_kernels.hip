@@ -32,6 +32,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "va_internal.hpp"
 
 namespace va {
@@ -1123,6 +1125,41 @@ __global__ void __launch_bounds__(kGatherWaves * 64) debug_gather_kernel(const c
       rows_out[(ustart + key) * kChunks + ch] =
           *reinterpret_cast<LDS_AS const u32x4*>(lds + tile_offset(ch, key));
   }
+}
+
+// ---------------------------------------------------------------------------
+// Fixed scratch for the allocation-free entry point: the same workspace
+// layout as a caller-owned workspace (chunk offsets, partial lse values,
+// fp16 partial outputs), in a device array of fixed size that each device
+// holds from the library's load until the process ends. Every call on a
+// device shares that device's copy (calls that overlap on one device race);
+// nothing in it has to start at zero, since every call writes what it reads.
+// In host code `scratch` names a host-side stand-in, never the device array:
+// its device address is looked up once per device and used instead.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with device `dev` current
+    if (e != hipSuccess) return e;
+    if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255) != 0) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

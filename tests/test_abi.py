@@ -147,3 +147,18 @@ def test_tree_accept_argument_checks(lib):
         args[i] = v
         assert lib.verify_attn_tree_accept(*args) == va.VA_EINVAL, (i, v)
 
+
+def test_noalloc_checks_on_the_host(lib):
+    args = [4096, 4096, 4096, 4096, 4096, 0.1, 4096, 4096, 1, 4, 8, 1024, 260, None]
+    bad = list(args)
+    bad[0] = None
+    assert lib.verify_attn_noalloc(*bad) == va.VA_EINVAL
+    bad = list(args)
+    bad[9] = 65                                   # Q > 64
+    assert lib.verify_attn_noalloc(*bad) == va.VA_EINVAL
+    big = list(args)
+    big[8:11] = [64, 16, 64]
+    big[12] = 64 * 100_000                        # needs more than the fixed scratch
+    assert lib.verify_attn_workspace_size(64, 16, 64, 64 * 100_000) > (64 << 20)
+    assert lib.verify_attn_noalloc(*big) == va.VA_ENOSPC
+    assert "scratch" in lib.verify_attn_last_error().decode()
