@@ -74,24 +74,20 @@ __device__ __forceinline__ int tile_offset(int chunk, int key) {
 // each per tile. One instruction fills one 1 KiB region (key group kg, line L):
 // lane l fetches, of key 8kg + l/8, the 16-byte chunk of line L that lands in
 // slot l%8 of the region, so every instruction moves 8 whole 128-byte lines.
-// Region ownership (gather wave j = 0..3):
-//   loads 0..4: key group j, lines 0, 1, 2, 3 and 8;
-//   loads 5..8: line 4 + j of key groups 0..3.
-// In the split kernel a tile slot is refilled while the previous tile's value
-// lines 4..7 may still be read, each by one wave only (value_line below); the
-// ownership above gives each of those lines to the wave that reads it, so
-// every refill waits for the reads of its own wave alone. The check after the
-// split kernel's layout constants proves this over the tables below.
+// Gather wave j owns key group j: all nine lines of keys 8j .. 8j + 7, so each
+// lane needs the pool slot of one key only. In the split kernel a tile slot is
+// refilled while other waves may still be reading the slot's previous tile
+// unless every read of that tile ends before the refill's phase barrier; the
+// check after the split kernel's layout constants proves, over the tables
+// below and the phase in which each wave reads its value lines, that no
+// refill overwrites a region another wave still reads.
 constexpr int kGatherWaves = kUnit / 8;
 constexpr int kGatherLoads = kRowBytes / 128;   // 9 load instructions per wave and tile
 constexpr int kKeyGroups = kUnit / 8;           // 4 groups of 8 keys per tile
-constexpr int kOwnLoads = 5;                    // loads 0..4 of gather wave j: key group j
-static_assert(kGatherWaves == kKeyGroups && kGatherLoads == kOwnLoads + kKeyGroups, "gather split");
+static_assert(kGatherWaves == kKeyGroups, "one gather wave per key group");
 
-__host__ __device__ constexpr int gather_kg(int j, int k) { return k < kOwnLoads ? j : k - kOwnLoads; }
-__host__ __device__ constexpr int gather_line(int j, int k) {
-  return k < 4 ? k : (k == 4 ? kGatherLoads - 1 : 4 + j);
-}
+__host__ __device__ constexpr int gather_kg(int j, int k) { return j + 0 * k; }
+__host__ __device__ constexpr int gather_line(int j, int k) { return k + 0 * j; }
 // Line of a tile whose value operands wave w reads (its 64 value dims are
 // chunks 8w .. 8w + 7; see value_chunk).
 __host__ __device__ constexpr int value_line(int w) { return w; }
@@ -101,15 +97,19 @@ __host__ __device__ constexpr int value_chunk(int w, int d, int g, int s) {
   return 8 * value_line(w) + 4 * d + 2 * (g & 1) + ((s & 3) >> 1);
 }
 
-// Slot indices of a tile reach LDS through one 4-byte direct load per lane:
-// lane l < 32 fetches the index of key slot_copy_key(l) to byte 4l of the
-// tile's 256-byte ring entry (lanes 32..63 repeat lanes 0..31 into bytes
-// 128..255), so that bytes 16r .. 16r+15 hold keys r, 8 + r, 16 + r, 24 + r:
-// one 16-byte read gives a gathering lane the slots of its key in all four
-// key groups.
-__host__ __device__ constexpr int slot_copy_key(int lane) { return 8 * (lane & 3) + ((lane & 31) >> 2); }
+struct GatherLane {
+  int key;   // key of the tile this lane fetches
+  int coff;  // byte offset of its chunk inside a 128-byte line
+  int kg;    // key group (region row)
+};
 
-typedef int i32x4g __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ GatherLane gather_lane(int gw, int lane) {
+  GatherLane g;
+  g.kg = gather_kg(gw, 0);
+  g.key = 8 * g.kg + (lane >> 3);
+  g.coff = ((lane & 7) ^ ((g.key >> 1) & 7)) * 16;
+  return g;
+}
 
 // Direct-to-LDS loads, written out in asm. (Issued through the builtin, an LDS
 // DMA anywhere in a wave's code makes the compiler wait for every LDS read of
@@ -131,28 +131,21 @@ __device__ __forceinline__ void lds_dma4(const void* gaddr, LDS_AS char* lds_dst
                : "=&s"(saved) : "v"(gaddr), "s"(lb) : "memory");
 }
 
-// Issue gather wave j's share of one tile gather (exactly kGatherLoads load
-// instructions, regions as in gather_kg / gather_line). slots[kg] is the pool
-// row of this lane's key 8kg + lane/8 (any out-of-range value for an absent
-// position: the zero row). The loads carry the nontemporal cache policy (nt):
-// a workgroup reads each row once, and with it one CU sustains about twice
-// the gather rate it reaches under the default policy.
-__device__ __forceinline__ void issue_tile_gather(const char* kv_pool, int64_t num_slots, i32x4g slots,
-                                                  LDS_AS char* tile, int j, int lane) {
-  const int r = lane >> 3, s = lane & 7;
-  // Chunk of the line that lands in slot s of a region: s ^ ((key >> 1) & 7)
-  // with key = 8kg + r, i.e. s ^ (4 (kg & 1) + r / 2).
-  auto row_of = [&](int kg) -> const char* {
-    const int32_t slot = kg == 0 ? slots[0] : kg == 1 ? slots[1] : kg == 2 ? slots[2] : slots[3];
-    const char* row = (slot >= 0 && slot < num_slots) ? kv_pool + (int64_t)slot * kRowBytes
-                                                      : reinterpret_cast<const char*>(g_zero_row);
-    return row + (s ^ (4 * (kg & 1) + (r >> 1))) * 16;
-  };
-  const char* own = row_of(gather_kg(j, 0));
+// Issue this wave's share of one tile gather (exactly kGatherLoads load
+// instructions, regions as in gather_kg / gather_line). `slot` is the pool row
+// of the lane's key (any out-of-range value for an absent position: the zero
+// row). The loads carry the nontemporal cache policy (nt): a workgroup reads
+// each row once, and with it one CU sustains about twice the gather rate it
+// reaches under the default policy.
+__device__ __forceinline__ void issue_tile_gather(const char* kv_pool, int64_t num_slots, int32_t slot,
+                                                  LDS_AS char* tile, const GatherLane& gl) {
+  const char* row = (slot >= 0 && slot < num_slots) ? kv_pool + (int64_t)slot * kRowBytes
+                                                    : reinterpret_cast<const char*>(g_zero_row);
+  row += gl.coff;
 #pragma unroll
   for (int k = 0; k < kGatherLoads; ++k) {
-    const int kg = gather_kg(j, k), L = gather_line(j, k);
-    lds_dma16_nt((k < kOwnLoads ? own : row_of(kg)) + L * 128, tile + (kg * 9 + L) * 1024);
+    const int L = gather_line(gl.kg, k);
+    lds_dma16_nt(row + L * 128, tile + (gl.kg * 9 + L) * 1024);
   }
 }
 
@@ -372,18 +365,21 @@ constexpr int kStageBytes = 32 * kStageRow;
 static_assert(kSplitWaves * kStageBytes <= kOffXchg, "epilogue staging fits in the tile ring");
 
 // The refill of a tile slot (gather of tile u + 3 in phase X of iteration u)
-// races with no read of the slot's previous tile u. After the barrier that
-// opens phase X, the only reads of tile u are the odd waves' value reads:
-// wave w >= 4 reads line value_line(w) of every key group. The even waves
-// read their value lines before that barrier and both halves read tile u's
-// score operands (lines 0..8) one iteration earlier. Gather wave j (wave 4 + j)
-// issues its loads only after its own value reads are complete, so each
-// region it writes must be one that no other wave reads after the barrier;
-// and the four gather waves together must write every region exactly once.
-// Both are checked here over the same tables the gather and the value reads
-// use.
+// must not overwrite a region that a wave still reads. The last reads of tile
+// u are the value reads: wave w reads line value_line(w) of every key group,
+// before the barrier that opens phase X (both halves; see the schedule in the
+// split kernel) unless values_read_in_phase_x(w) says otherwise; both halves
+// read tile u's score operands (lines 0..8) one iteration earlier. Gather wave
+// j (wave 4 + j) issues its loads after its own value reads are complete, so
+// each region it writes must be one that no other wave reads after the
+// barrier; and the four gather waves together must write every region
+// exactly once. Both are checked here over the same tables the gather and the
+// value reads use. (Letting the odd waves read their values in phase X, with
+// each gather wave writing all nine lines of its key group, fails the check:
+// a refill would overwrite value lines that other odd waves still read.)
+__host__ __device__ constexpr bool values_read_in_phase_x(int wave) { return wave < 0; }
 __host__ __device__ constexpr bool read_after_phase_barrier(int wave, int line) {
-  return wave >= kSplitWaves / 2 && value_line(wave) == line;
+  return values_read_in_phase_x(wave) && value_line(wave) == line;
 }
 __host__ __device__ constexpr bool gather_ownership_ok() {
   int cover[kKeyGroups][kGatherLoads] = {};
@@ -404,11 +400,6 @@ __host__ __device__ constexpr bool gather_ownership_ok() {
       for (int g = 0; g < 4; ++g)
         for (int s = 0; s < 16; ++s)
           if (value_chunk(w, d, g, s) / 8 != value_line(w)) return false;
-  // the slot ring: byte 4l of an entry holds key slot_copy_key(l); a gathering
-  // lane reads bytes 16r + 4kg for key 8kg + r (and lanes 32..63 repeat 0..31)
-  for (int r = 0; r < 8; ++r)
-    for (int kg = 0; kg < kKeyGroups; ++kg)
-      if (slot_copy_key(4 * r + kg) != 8 * kg + r || slot_copy_key(32 + 4 * r + kg) != 8 * kg + r) return false;
   return true;
 }
 static_assert(gather_ownership_ok(), "a tile refill may overwrite a region another wave still reads");
@@ -525,47 +516,39 @@ split_kernel(SplitArgs a) {
   LDS_AS char* abuf = lds + kOffAlpha;
   LDS_AS char* fbuf = lds + kOffFlag;
 
-  // Gather bookkeeping (see issue_tile_gather): the odd half (waves 4-7)
-  // issues all direct-to-LDS loads, nine per wave and tile; lane l always
-  // fetches key l/8 of each key group it covers. The even half issues none
-  // inside the loop, so its LDS reads never wait on them.
-  // (Per-lane values are re-derived from fresh_lane() at each use, so they
-  // do not occupy registers across the loop.)
+  // Gather bookkeeping (see gather_lane): the odd half (waves 4-7) issues all
+  // direct-to-LDS loads, nine per wave and tile; lane l always fetches the
+  // same key of a tile. The even half issues none inside the loop, so its
+  // LDS reads never wait on them.
+  // (The per-lane gather fields are re-derived from fresh_lane() at each use,
+  // so they do not occupy registers across the loop.)
+  auto glane = [&]() { return gather_lane(wave - kSplitWaves / 2, fresh_lane()); };
   // Slot indices travel through LDS like the latent rows: wave 4 copies the
   // 32 kv_indices entries of tile v into ring entry v % 8 with one
-  // direct-to-LDS dword load (in slot_copy_key order), kSlotAhead tiles ahead,
-  // so that the vmcnt waits that cover the gathers cover them too. (A
-  // register load would make the compiler wait for it with a vmcnt that also
-  // drains the gathers issued after it.)
+  // direct-to-LDS dword load (lanes 32-63 duplicate lanes 0-31), kSlotAhead
+  // tiles ahead, so that the vmcnt waits that cover the gathers cover them
+  // too. (A register load would make the compiler wait for it with a vmcnt
+  // that also drains the gathers issued after it.)
   LDS_AS char* slot_ring = lds + kOffSlots;
+  auto tile_key_ok = [&](int v, int gkey) -> bool { return kstart + (int64_t)v * kUnit + gkey < kend; };
   auto load_slots_to_lds = [&](int v) {
     if (wave == 4) {
-      int64_t gpos = sbase + kstart + (int64_t)v * kUnit + slot_copy_key(lane);
+      int64_t gpos = sbase + kstart + (int64_t)v * kUnit + (lane & 31);
       gpos = gpos < a.total_kv ? gpos : a.total_kv - 1;
       gpos = gpos < 0 ? 0 : gpos;
       lds_dma4(a.kv_indices + gpos, slot_ring + (v % kSlotRing) * 256);
     }
   };
-  // Slots of this lane's key r = lane/8 in the four key groups of tile v
-  // (-1, the zero row, for keys past the chunk).
-  auto read_slots = [&](int v) -> i32x4g {
-    const int r = fresh_lane() >> 3;
-    i32x4g sl = *reinterpret_cast<LDS_AS const i32x4g*>(slot_ring + (v % kSlotRing) * 256 + r * 16);
-    const int64_t k0 = kstart + (int64_t)v * kUnit + r;
-#pragma unroll
-    for (int kg = 0; kg < kKeyGroups; ++kg) sl[kg] = k0 + 8 * kg < kend ? sl[kg] : -1;
-    return sl;
+  auto read_slot = [&](int v) -> int32_t {
+    const int gkey = glane().key;
+    const int32_t sl = *reinterpret_cast<LDS_AS const int32_t*>(slot_ring + (v % kSlotRing) * 256 + gkey * 4);
+    return tile_key_ok(v, gkey) ? sl : -1;
   };
-  auto load_slots = [&](int v) -> i32x4g {
-    const int64_t k0 = kstart + (int64_t)v * kUnit + (fresh_lane() >> 3);
-    i32x4g sl;
-#pragma unroll
-    for (int kg = 0; kg < kKeyGroups; ++kg) sl[kg] = k0 + 8 * kg < kend ? a.kv_indices[sbase + k0 + 8 * kg] : -1;
-    return sl;
+  auto load_slot = [&](int v) -> int32_t {
+    const int64_t pos = kstart + (int64_t)v * kUnit + glane().key;
+    return pos < kend ? a.kv_indices[sbase + pos] : -1;
   };
-  auto issue = [&](i32x4g slots, LDS_AS char* tile) {
-    issue_tile_gather(a.kv_pool, a.num_slots, slots, tile, wave - kSplitWaves / 2, fresh_lane());
-  };
+  auto issue = [&](int32_t slot, LDS_AS char* tile) { issue_tile_gather(a.kv_pool, a.num_slots, slot, tile, glane()); };
 
   // Online-softmax state of the pair's rows (log2 domain; kept by the even
   // half) and this wave's output accumulators O^T: [row block][value block].
@@ -755,13 +738,16 @@ split_kernel(SplitArgs a) {
   // core:
   //   phase Y: the even wave runs the softmax of tile u (vector ALU) while the
   //            odd wave applies tile u-1 to its values and computes its
-  //            partial scores of tile u+1 (34 MFMAs); the even wave then
-  //            reads its value operands of tile u;
+  //            partial scores of tile u+1 (34 MFMAs); both then read their
+  //            value operands of tile u, the last reads of tile u;
   //   phase X: the even wave applies tile u and computes its partial scores
-  //            of tile u+1 (34 MFMAs) while the odd wave reads its value
-  //            operands of tile u (which frees tile u's ring slot), hands over
-  //            its partial scores, issues the gather of tile u+3 into the
-  //            freed slot, and waits for tile u+2.
+  //            of tile u+1 (34 MFMAs) while the odd wave hands over its
+  //            partial scores, issues the gather of tile u+3 into tile u's
+  //            slot (nobody reads it after the barrier that opens phase X),
+  //            and waits for tile u+2.
+  // (With the odd wave's value reads in phase X, where it has slack, the
+  // split kernel ran 2% faster, but its gather then overwrote value lines that
+  // other odd waves could still be reading; see gather_ownership_ok.)
   // P, the rescale factors and flags are double-buffered by tile parity, as
   // the odd half reads those of tile u-1 while the even half writes tile u's.
   auto run = [&](auto pc) {
@@ -777,9 +763,9 @@ split_kernel(SplitArgs a) {
     // half: queries and mask row.
     u32x4 qv[kHalfKSteps];
     if constexpr (PP == 1) {
-      const i32x4g s0 = load_slots(0);
-      const i32x4g s1 = load_slots(1);
-      const i32x4g s2 = load_slots(2);
+      const int32_t s0 = load_slot(0);
+      const int32_t s1 = load_slot(1);
+      const int32_t s2 = load_slot(2);
       load_q(qv);
       place_q(qv);
       issue(s0, lds);
@@ -820,12 +806,15 @@ split_kernel(SplitArgs a) {
         else sa = f32x16{};
         __builtin_amdgcn_s_setprio(0);
       }
+      constexpr bool kValuesInX = values_read_in_phase_x(PP * kSplitWaves / 2);
+      static_assert(!values_read_in_phase_x(0), "the even half applies tile u in phase X");
       f16x8 va[kWaveDvBlocks][2];
-      if constexpr (PP == 0) read_values(tile, va);
+      if constexpr (!kValuesInX) read_values(tile, va);
       if constexpr (PP == 0) {
         // The even wave converts its values before the barrier: its phase Y
-        // has slack, its phase X does not. (The odd wave reads and converts
-        // its values of tile u in phase X, where it has slack.)
+        // has slack, its phase X does not. (The odd wave's conversion is left
+        // to the compiler, which sinks it into phase X, where the odd wave
+        // has slack.)
 #pragma unroll
         for (int db = 0; db < kWaveDvBlocks; ++db) asm volatile("" ::"v"(va[db][0]), "v"(va[db][1]));
       }
@@ -843,16 +832,23 @@ split_kernel(SplitArgs a) {
         __builtin_amdgcn_s_setprio(0);
         asm volatile("s_barrier" ::: "memory");
       } else {
-        // the odd wave reads its values of tile u here, where it has slack
-        read_values(tile, vheld);
+        if constexpr (kValuesInX) {
+          read_values(tile, vheld);
+        } else {
+#pragma unroll
+          for (int db = 0; db < kWaveDvBlocks; ++db) {
+            vheld[db][0] = va[db][0];
+            vheld[db][1] = va[db][1];
+          }
+        }
         if (more) write_xchg(sa);
         load_slots_to_lds(u + kSlotAhead);
-        const i32x4g slots = read_slots(u + kGatherAhead);
-        // The refill of tile u's slot with tile u + 3 writes, besides regions
-        // nobody reads after the phase barrier, only this wave's own value
-        // line (gather_ownership_ok), so it waits for this wave's reads alone.
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        issue(slots, tile);
+        const int32_t slot = read_slot(u + kGatherAhead);
+        // The refill of tile u's slot with tile u + 3 may overwrite only what
+        // nobody reads any more (gather_ownership_ok): after the barrier that
+        // opened this phase, at most this wave's own value reads.
+        if constexpr (kValuesInX) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue(slot, tile);
         // Tile u+2 has landed once no more than the loads issued after it are
         // outstanding: this phase's slot copy (wave 4) and its nine gather
         // loads. (The compiler does not track direct-to-LDS loads, so the wait
@@ -1091,9 +1087,9 @@ __global__ void __launch_bounds__(256) merge_few_kernel(const _Float16* __restri
 
 // ---------------------------------------------------------------------------
 // Debug gather: the split kernel's slot copy and gather routines for one
-// tile per workgroup (wave 0 copies the 32 slot indices into LDS in
-// slot_copy_key order, each of the four waves reads its lanes' slots back and
-// issues its share of the gather), copied back out in position order.
+// tile per workgroup (wave 0 copies the 32 slot indices into LDS, each of the
+// four waves reads its lanes' slots back and issues its share of the gather),
+// copied back out in position order.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(kGatherWaves * 64) debug_gather_kernel(const char* __restrict__ kv_pool,
                                                                          const int32_t* __restrict__ kv_indices,
@@ -1106,17 +1102,15 @@ __global__ void __launch_bounds__(kGatherWaves * 64) debug_gather_kernel(const c
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t ustart = (int64_t)blockIdx.x * kUnit;
   if (wave == 0) {
-    int64_t pos = ustart + slot_copy_key(lane);
+    int64_t pos = ustart + (lane & 31);
     pos = pos < n ? pos : n - 1;
     lds_dma4(kv_indices + pos, ring);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   __syncthreads();
-  const int r = lane >> 3;
-  i32x4g sl = *reinterpret_cast<LDS_AS const i32x4g*>(ring + r * 16);
-#pragma unroll
-  for (int kg = 0; kg < kKeyGroups; ++kg) sl[kg] = ustart + 8 * kg + r < n ? sl[kg] : -1;
-  issue_tile_gather(kv_pool, num_slots, sl, lds, wave, lane);
+  const GatherLane gl = gather_lane(wave, lane);
+  const int32_t sl = *reinterpret_cast<LDS_AS const int32_t*>(ring + gl.key * 4);
+  issue_tile_gather(kv_pool, num_slots, ustart + gl.key < n ? sl : -1, lds, gl);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int p = tid; p < kUnit * kChunks; p += kGatherWaves * 64) {
