@@ -66,7 +66,7 @@ __device__ __attribute__((aligned(16))) uint32_t g_zero_row[kRowBytes / 4] = {0}
 // inside a region, key k%8 owns 8 slots and chunk c%8 sits at slot
 // (c%8) ^ ((k >> 1) & 7). The xor spreads both the score reads (32 keys, one
 // chunk) and the value transpose reads over all banks.
-__device__ __forceinline__ int tile_offset(int chunk, int key) {
+__host__ __device__ constexpr int tile_offset(int chunk, int key) {
   return ((key >> 3) * 9 + (chunk >> 3)) * 1024 + ((key & 7) * 8 + ((chunk & 7) ^ ((key >> 1) & 7))) * 16;
 }
 
@@ -96,6 +96,49 @@ __host__ __device__ constexpr int value_line(int w) { return w; }
 __host__ __device__ constexpr int value_chunk(int w, int d, int g, int s) {
   return 8 * value_line(w) + 4 * d + 2 * (g & 1) + ((s & 3) >> 1);
 }
+
+// Score A operand: A-row n of a 32x32x16 block holds key arow_key(n) (bits 2
+// and 3 of n swapped), so that the score accumulator element i of lane
+// (n + 32h) is key 16*(i/8) + 8h + (i%8), the B-operand layout of P. K-step ks
+// of dim half p reads chunk 2(18p + ks) + h; within the 1 KiB region of a key
+// group and line, the swizzle of tile_offset only flips slot bits (4..6) of
+// the offset, so k-steps j = 0..3 follow from k-step 0 by an XOR (and, in dim
+// half 1, k-steps 2 and 3 lie in the next region); k-step j + 4q adds q KiB.
+__host__ __device__ constexpr int arow_key(int n) { return (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1); }
+__host__ __device__ constexpr int score_koff(int a0, int j, int p) {
+  return (a0 ^ (32 * j)) + ((p == 1 && j >= 2) ? 1024 : 0);
+}
+// Value transpose read (hf, d) from read (0, 0): key 4hf further (+512 bytes)
+// flips slot bit 1, value block d flips slot bit 2.
+__host__ __device__ constexpr int value_off(int t00, int hf, int d) { return ((t00 + 512 * hf) ^ (32 * hf)) ^ (64 * d); }
+// Both derivations reproduce tile_offset for every lane, wave and dim half.
+// (Tile bases are multiples of 1 KiB, so the XORs may act on absolute LDS
+// addresses as well as on offsets.)
+__host__ __device__ constexpr bool lane_offsets_ok() {
+  for (int p = 0; p < 2; ++p)
+    for (int lane = 0; lane < 64; ++lane) {
+      const int nn = lane & 31, hh = lane >> 5;
+      const int a0 = tile_offset(36 * p + hh, arow_key(nn));
+      for (int j = 0; j < 4; ++j)
+        for (int q = 0; q < 5; ++q) {
+          if (4 * q + j >= 18) continue;
+          if (tile_offset(2 * (18 * p + 4 * q + j) + hh, arow_key(nn)) != score_koff(a0, j, p) + 1024 * q) return false;
+        }
+    }
+  for (int w = 0; w < 8; ++w)
+    for (int lane = 0; lane < 64; ++lane) {
+      const int g = lane >> 4, s = lane & 15, hh = lane >> 5;
+      const int t00 = tile_offset(value_chunk(w, 0, g, s), 8 * hh + (s >> 2)) + (s & 1) * 8;
+      for (int hf = 0; hf < 2; ++hf)
+        for (int d = 0; d < 2; ++d)
+          for (int t = 0; t < 2; ++t)
+            if (tile_offset(value_chunk(w, d, g, s), 16 * t + 8 * hh + 4 * hf + (s >> 2)) + (s & 1) * 8 !=
+                value_off(t00, hf, d) + 18432 * t)
+              return false;
+    }
+  return (kUnit * kRowBytes) % 1024 == 0;
+}
+static_assert(lane_offsets_ok(), "derived LDS operand offsets differ from tile_offset");
 
 struct GatherLane {
   int key;   // key of the tile this lane fetches
@@ -492,24 +535,27 @@ split_kernel(SplitArgs a) {
   // accumulator element i of lane (n + 32h) is key 16*(i/8) + 8h + (i%8).
   // Its k-step ks of this wave reads chunk 2(18p + ks) + h; a_off[j] is the
   // address for ks = j, and ks = j + 4q adds q KiB.
-  auto score_offsets = [&](int (&a_off)[4]) {
+  // Only the offset of k-step 0 is computed; the others follow by score_koff
+  // (lane_offsets_ok).
+  auto score_offsets = [&](LDS_AS const char* tile, unsigned (&a_addr)[4]) {
     const int fl = fresh_lane();
-    const int nn = fl & 31, hh = fl >> 5;
-    const int arow_key = (nn & ~12) | ((nn & 4) << 1) | ((nn & 8) >> 1);
+    const int a0 = tile_offset(2 * kHalfKSteps * p + (fl >> 5), arow_key(fl & 31));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) a_off[j] = tile_offset(2 * (kHalfKSteps * p + j) + hh, arow_key);
+    for (int j = 0; j < 4; ++j) a_addr[j] = (unsigned)(uintptr_t)tile + (unsigned)score_koff(a0, j, p);
   };
   // Value transpose reads: group g = lane/16, s = lane%16 supplies the address
   // of V[key 16t + 8h + 4hf + s/4][dv 32db + 16(g%2) + 4(s%4) .. +3] for this
-  // wave's blocks db = 2w + d; key 16t adds 18 KiB (t is an immediate).
-  auto value_offsets = [&](int (&tr_off)[2][2]) {
+  // wave's blocks db = 2w + d; key 16t adds 18 KiB (t is an immediate). Only
+  // the offset for (hf, d) = (0, 0) is computed; the others follow by
+  // value_off (lane_offsets_ok).
+  auto value_offsets = [&](LDS_AS const char* tile, unsigned (&tr_addr)[2][2]) {
     const int fl = fresh_lane();
     const int g = fl >> 4, s = fl & 15, hh = fl >> 5;
+    const int t00 = tile_offset(value_chunk(wave, 0, g, s), 8 * hh + (s >> 2)) + (s & 1) * 8;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-      for (int d = 0; d < 2; ++d)
-        tr_off[hf][d] = tile_offset(value_chunk(wave, d, g, s), 8 * hh + 4 * hf + (s >> 2)) + (s & 1) * 8;
+      for (int d = 0; d < 2; ++d) tr_addr[hf][d] = (unsigned)(uintptr_t)tile + (unsigned)value_off(t00, hf, d);
   };
   LDS_AS char* xchg = lds + kOffXchg + pair * kXchgBytes + lane * 16;   // + k * 1024
   LDS_AS char* pbuf = lds + kOffP + lane * 16;                          // + rb * kPBytes + t * 1024
@@ -615,12 +661,12 @@ split_kernel(SplitArgs a) {
   // its use, which would expose one LDS round trip per MFMA.
   auto scores = [&](LDS_AS const char* tile) -> f32x16 {
     f32x16 acc = f32x16{};
-    int a_off[4];
-    score_offsets(a_off);
+    unsigned a_addr[4];
+    score_offsets(tile, a_addr);
     constexpr int kDepth = 4;    // K reads in flight
     constexpr int kQDepth = 2;   // parked-query reads in flight
     auto kload = [&](int ks) {
-      return *reinterpret_cast<LDS_AS const bf16x8*>(tile + a_off[ks & 3] + (ks >> 2) * 1024);
+      return *reinterpret_cast<LDS_AS const bf16x8*>((uintptr_t)(a_addr[ks & 3] + (ks >> 2) * 1024));
     };
     auto qpark = [&](int ks) {
       return *reinterpret_cast<LDS_AS const bf16x8*>(my_q + (ks - kRegKSteps) * 1024);
@@ -706,12 +752,12 @@ split_kernel(SplitArgs a) {
   // the compiler fence them).
   auto read_values = [&](LDS_AS const char* tile, f16x8 (&va)[kWaveDvBlocks][2]) {
     u32x2 v[kWaveDvBlocks][2][2];   // [d][t][hf]
-    int tr_off[2][2];
-    value_offsets(tr_off);
-    const unsigned a00 = (unsigned)(uintptr_t)(tile + tr_off[0][0]);
-    const unsigned a10 = (unsigned)(uintptr_t)(tile + tr_off[1][0]);
-    const unsigned a01 = (unsigned)(uintptr_t)(tile + tr_off[0][1]);
-    const unsigned a11 = (unsigned)(uintptr_t)(tile + tr_off[1][1]);
+    unsigned tr_addr[2][2];
+    value_offsets(tile, tr_addr);
+    const unsigned a00 = tr_addr[0][0];
+    const unsigned a10 = tr_addr[1][0];
+    const unsigned a01 = tr_addr[0][1];
+    const unsigned a11 = tr_addr[1][1];
     auto tr = [&](unsigned addr) {
       const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(uintptr_t)addr);
       return __builtin_bit_cast(u32x2, r);
