@@ -54,8 +54,11 @@ hipError_t launch_split(const SplitArgs& a, int grid, hipStream_t stream);
 constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
 hipError_t noalloc_scratch(void** ptr);
 // The merge: the one-wave-per-row form when the partial buffers hold at most
-// kMergeFewPerSeq chunks per sequence on average, else the chunk-lane form.
+// kMergeFewPerSeq chunks per sequence on average, the slice form when they hold
+// at least kMergeSlicePerSeq (few rows, many chunks: the 8-head shape), else
+// the chunk-lane form.
 constexpr int kMergeFewPerSeq = 16;
+constexpr int kMergeSlicePerSeq = 64;
 hipError_t launch_merge(const _Float16* part_o, const float* part_lse, const int32_t* chunk_off,
                         float* out, float* lse, int B, int R, int max_chunks, hipStream_t stream);
 hipError_t launch_debug_gather(const void* kv_pool, const int32_t* kv_indices, int64_t n,

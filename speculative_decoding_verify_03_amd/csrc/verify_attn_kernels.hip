@@ -1069,6 +1069,100 @@ __global__ void __launch_bounds__(256) merge_kernel(const _Float16* __restrict__
 }
 
 // ---------------------------------------------------------------------------
+// Merge for sequences with many chunks: one 256-thread workgroup per (row,
+// 64-dim slice of the 512 value dims), so that each 128-byte line of a chunk's
+// partial row is read by exactly one workgroup and there are eight workgroups
+// per row. Thread t takes 8 dims (one 16-byte load per chunk) and chunk lane
+// t / 8 of 32: chunks c0 + lane + 32k, loaded eight at a time before any is
+// folded, so that every thread keeps several independent loads in flight (the
+// merge is bound by memory latency, not by its arithmetic). Each lane folds its
+// chunks with a running maximum (log2 domain); an LDS step combines the 32
+// lanes.
+// ---------------------------------------------------------------------------
+constexpr int kSliceLanes = 32;   // chunk lanes per workgroup
+constexpr int kSliceBatch = 8;    // chunks per lane and load batch
+constexpr int kSlices = kValue / 64;
+
+__global__ void __launch_bounds__(256) merge_slice_kernel(const _Float16* __restrict__ part_o,
+                                                          const float* __restrict__ part_lse,
+                                                          const int32_t* __restrict__ chunk_off,
+                                                          float* __restrict__ out, float* __restrict__ lse,
+                                                          int B, int R) {
+  __shared__ float s_acc[kSliceLanes][64];
+  __shared__ float s_m[kSliceLanes];
+  __shared__ float s_w[kSliceLanes];
+  const int64_t grow = (int64_t)(blockIdx.x / kSlices);
+  const int slice = blockIdx.x % kSlices;
+  if (grow >= (int64_t)B * R) return;
+  const int b = (int)(grow / R);
+  const int r = (int)(grow - (int64_t)b * R);
+  const int t = threadIdx.x;
+  const int dl = t & 7, cl = t >> 3;
+  const int c0 = chunk_off[b], c1 = chunk_off[b + 1];
+  const _Float16* obase = part_o + (int64_t)r * kValue + slice * 64 + dl * 8;
+  float m = -INFINITY, ws = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int cs = c0 + cl; cs < c1; cs += kSliceLanes * kSliceBatch) {
+    float l[kSliceBatch];
+    f16x8 v[kSliceBatch];
+#pragma unroll
+    for (int k = 0; k < kSliceBatch; ++k) {
+      const int ck = cs + k * kSliceLanes;
+      l[k] = -INFINITY;   // past the row's last chunk: no load, weight 0
+      v[k] = f16x8{};
+      if (ck < c1) {
+        l[k] = part_lse[(int64_t)ck * R + r] * kLog2e;
+        v[k] = *reinterpret_cast<const f16x8*>(obase + (int64_t)ck * R * kValue);
+      }
+    }
+    float mb = m;
+#pragma unroll
+    for (int k = 0; k < kSliceBatch; ++k) mb = fmaxf(mb, l[k]);
+    if (mb > -INFINITY) {
+      const float sc = __builtin_amdgcn_exp2f(m - mb);   // 0 while nothing was folded
+      ws *= sc;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] *= sc;
+#pragma unroll
+      for (int k = 0; k < kSliceBatch; ++k) {
+        const float w = __builtin_amdgcn_exp2f(l[k] - mb);   // 0 for an empty chunk
+        ws += w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += w * (float)v[k][e];
+      }
+      m = mb;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s_acc[cl][dl * 8 + e] = acc[e];
+  if (dl == 0) {
+    s_m[cl] = m;
+    s_w[cl] = ws;
+  }
+  __syncthreads();
+  if (t < 64) {
+    float M = s_m[0];
+#pragma unroll
+    for (int k = 1; k < kSliceLanes; ++k) M = fmaxf(M, s_m[k]);
+    float* orow = out + grow * kValue + slice * 64 + t;
+    if (!(M > -INFINITY)) {   // no chunk, or nothing visible in any chunk
+      *orow = 0.f;
+      if (t == 0 && slice == 0) lse[grow] = -INFINITY;
+      return;
+    }
+    float tot = 0.f, wt = 0.f;
+#pragma unroll
+    for (int k = 0; k < kSliceLanes; ++k) {
+      const float sc = __builtin_amdgcn_exp2f(s_m[k] - M);   // 0 for a lane with no visible chunk
+      tot += sc * s_acc[k][t];
+      wt += sc * s_w[k];
+    }
+    *orow = tot * (1.f / wt);
+    if (t == 0 && slice == 0) lse[grow] = (M + __builtin_amdgcn_logf(wt)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Merge for batches whose sequences have few chunks each: one wave per (row,
 // half of the 512 value dims), lane l holding 4 dims, with no cross-lane
 // step. The wave loads the partials of up to eight chunks at once and folds
@@ -1215,6 +1309,9 @@ hipError_t launch_merge(const _Float16* part_o, const float* part_lse, const int
   const int64_t rows = (int64_t)B * R;
   if (max_chunks <= kMergeFewPerSeq * B) {   // few chunks per sequence on average
     hipLaunchKernelGGL(merge_few_kernel, dim3((unsigned)((rows * 2 + 3) / 4)), dim3(256), 0, stream, part_o,
+                       part_lse, chunk_off, out, lse, B, R);
+  } else if (max_chunks >= kMergeSlicePerSeq * B) {   // many chunks per sequence
+    hipLaunchKernelGGL(merge_slice_kernel, dim3((unsigned)(rows * kSlices)), dim3(256), 0, stream, part_o,
                        part_lse, chunk_off, out, lse, B, R);
   } else {
     hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(rows * 4)), dim3(256), 0, stream, part_o,

@@ -90,6 +90,21 @@ def test_many_small_chunks_cross_the_tail(env):
         _check(env, w, label=f"chunk{chunk}", chunk_keys=chunk)
 
 
+def test_many_chunks_per_sequence_slice_merge(env):
+    """32-key chunks over ragged sequences give at least 64 chunks per sequence on
+    average, so the merge runs in its slice form (one workgroup per row and 64-dim
+    slice, 32 chunk lanes): sequences with 126, 1 and 79 chunks, one without prefix,
+    and a query with nothing visible."""
+    tm = np.stack([np.tril(np.ones((4, 4), np.uint8))] * 3)
+    tm[1, 2, :] = 0                       # sequence 1 has no prefix: query 2 sees nothing
+    w = make_workload("slice", [308], B=3, Q=4, H=40, prefix_lens=[4000, 0, 2500], mask=tm, num_slots=8000)
+    torch, va = env
+    plan = va.query_plan(w.B, w.Q, w.H, w.total_kv, chunk_keys=32)
+    assert plan["max_chunks"] >= 64 * w.B
+    out, lse = _check(env, w, label="slice_merge", chunk_keys=32)
+    assert np.all(np.isneginf(lse[1, 2])) and np.all(out[1, 2] == 0)
+
+
 def test_out_of_range_slots_read_as_zero_rows(env):
     w = make_workload("oob", [303], B=2, Q=4, H=8, prefix_lens=[50, 9], mask="tree", num_slots=128)
     bad = w.kv_indices.copy()
