@@ -284,7 +284,7 @@ def summarize_trace(path: str, config: str, warmup: int, steps: int) -> str:
         for name, lst in (("split_kernel", split), (merge[0]["Kernel_Name"].split("(")[0], merge)):
             d = np.array([dur(lst[i]) for i in sel])
             stats[(name, kind)] = d
-            short = "merge_few_kernel" if "few" in name else ("merge_kernel" if "merge" in name else name)
+            short = next((k for k in ("split_kernel", "merge_few_kernel", "merge_slice_kernel", "merge_kernel") if k in name), name)
             out.append(f"| {short} | {len(d)} | {kind} | {d.mean():.2f} | {d.min():.2f} | {d.max():.2f} |")
         calls = np.array([(int(merge[i]["End_Timestamp"]) - int(split[i]["Start_Timestamp"])) / 1e3 for i in sel])
         out.append(f"| whole call (split start to merge end) | {len(calls)} | {kind} | {calls.mean():.2f} | "
