@@ -492,7 +492,10 @@ split_kernel(SplitArgs a) {
   const int rr = row_ok ? r : 0;
   // Tail-visibility bits of the lane's query (even half; all ones elsewhere).
   // The first 16 positions are 16 unconditional byte loads (indices clamped
-  // into the row), so they cost one memory round trip, not one each.
+  // into the row), so they cost one memory round trip, not one each. Only a
+  // chunk that reaches the tail (kend > P) consults them, and only such a
+  // chunk loads them: at the start of a launch the byte loads add about two
+  // microseconds to every workgroup that issues them.
   uint64_t tbits = ~0ull;
   auto load_mask = [&]() {
     const uint8_t* mrow = a.tree_mask + ((int64_t)b * a.Q + rr / a.H) * a.Q;
@@ -821,7 +824,7 @@ split_kernel(SplitArgs a) {
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kGatherLoads) : "memory");
     } else {
       load_q(qv);
-      load_mask();
+      if (kend > P) load_mask();   // uniform across the workgroup
       place_q(qv);
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
