@@ -105,6 +105,30 @@ def test_many_chunks_per_sequence_slice_merge(env):
     assert np.all(np.isneginf(lse[1, 2])) and np.all(out[1, 2] == 0)
 
 
+def test_prefix_length_past_the_array(env):
+    """A prefix length larger than the array holds (prefix_lens[0] + Q > total_kv):
+    the header's rule is that positions past total_kv are absent, so every one of
+    the total_kv positions counts as prefix and is visible to every query. The plan
+    then has a last chunk that lies wholly past the array (it must still get a
+    workgroup and leave an empty partial). Expected: the oracle on the same rows
+    with the last Q positions as a fully visible tail, which is the same visible
+    set."""
+    torch, va = env
+    w = make_workload("past", [311], B=1, Q=8, H=16, prefix_lens=[3000], mask="chain", num_slots=4096)
+    assert w.total_kv == 3008 and w.total_kv % 32 == 0
+    d = upload(w)
+    d["prefix_lens"].fill_(w.total_kv)    # claims 3008 prefix positions + 8 tail positions
+    ref = oracle.verify_attention(w.q, w.kv_pool, w.kv_indices, w.prefix_lens,
+                                  np.ones_like(w.tree_mask), w.scale)
+    for chunk in (0, 32):                 # the automatic plan, and one chunk per tile
+        if chunk:
+            plan = va.query_plan(w.B, w.Q, w.H, w.total_kv, chunk_keys=chunk)
+            assert plan["grid"] >= (w.total_kv + w.Q + chunk - 1) // chunk
+        out, lse = run_gpu(va, d, w.scale, chunk_keys=chunk)
+        m = compare(out, lse, *ref, f"past{chunk}")
+        print(f"[parity] past{chunk}: {m}", flush=True)
+
+
 def test_out_of_range_slots_read_as_zero_rows(env):
     w = make_workload("oob", [303], B=2, Q=4, H=8, prefix_lens=[50, 9], mask="tree", num_slots=128)
     bad = w.kv_indices.copy()
