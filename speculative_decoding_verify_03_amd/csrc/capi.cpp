@@ -3,7 +3,8 @@
 // kernel). The ABI is declared in include/verify_attn.h and, for tests and
 // measurement, include/verify_attn_testing.h. No entry point allocates,
 // synchronises or reads device memory on the host, and none keeps state
-// between calls other than a per-device cache of the compute-unit count.
+// between calls other than a per-device cache of the compute-unit count (and,
+// for verify_attn_noalloc, the fixed device scratch and its address).
 
 #include <hip/hip_runtime.h>
 
