@@ -133,8 +133,20 @@ def cpu_baseline(w, heads, min_seconds=10.0, max_reps=20):
         "cores": blas_threads if blas_threads else len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": f"oracle.verify_attention on the same workload ({what}), {reps} calls in "
-                  f"{total:.1f} s; host has {len(os.sched_getaffinity(0))} usable cores",
+                  f"{total:.1f} s; host has {len(os.sched_getaffinity(0))} usable cores ({cpu_model()})",
     }
+
+
+def cpu_model() -> str:
+    """The host CPU's model name, as /proc/cpuinfo gives it (or 'unknown CPU')."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
 
 
 class Evictor:
