@@ -78,6 +78,20 @@ def test_bad_arguments_rejected_before_launch(lib, over, code):
     assert lib.verify_attn_last_error().decode() != ""
 
 
+def test_plan_grid_covers_every_chunk(lib):
+    """The grid gives row_tiles workgroups to every chunk the device plan can
+    produce, rounded up to groups of 8 chunks: for one sequence
+    ceil((total_kv + Q) / chunk_keys) chunks (its N is at most total_kv + Q and its
+    chunk length at least chunk_keys), for a batch the partial buffers' capacity."""
+    for B, Q, H, T, ck in [(1, 16, 64, 185016, 0), (1, 16, 8, 185016, 0), (1, 16, 64, 4112, 0),
+                           (1, 8, 16, 3008, 32), (1, 4, 8, 260, 0), (8, 8, 64, 528448, 0), (3, 4, 40, 6512, 32)]:
+        p = va.query_plan(B, Q, H, T, chunk_keys=ck)
+        L = p["chunk_keys"]
+        need = -(-(T + Q) // L) if B == 1 else p["max_chunks"]
+        assert need <= p["max_chunks"]
+        assert p["grid"] == -(-need // 8) * 8 * p["row_tiles"], (B, Q, H, T, ck, p)
+
+
 def test_debug_gather_argument_checks(lib):
     assert lib.verify_attn_debug_gather(None, None, 0, 1, None, None) == va.VA_OK
     assert lib.verify_attn_debug_gather(None, 4096, 5, 10, 4096, None) == va.VA_EINVAL
