@@ -91,14 +91,17 @@ bool make_plan(int B, int Q, int H, int64_t total_kv, int ncu, int32_t chunk_key
   if (max_chunks > INT32_MAX / 8) return false;
   p->max_chunks = (int32_t)max_chunks;
   // Workgroups: the row tiles of every chunk the kernel's plan can produce,
-  // rounded up to whole groups of 8 chunks (the XCD mapping). A batch of one
-  // sequence has at most ceil((total_kv + Q) / ideal) chunks (its N is at
-  // most total_kv + Q, its chunk length at least ideal), which is below the
-  // buffer capacity; launching no workgroup beyond it matters because a
-  // surplus workgroup only gets a compute unit once a working one has
-  // finished, and then adds its own start-up to the end of the launch.
+  // rounded up to whole groups of 8 chunks (the XCD mapping). When the plan
+  // searches a chunk length (a budget above B, at most kPlanThreads
+  // sequences) it produces at most `target` chunks; a batch of one sequence
+  // has at most ceil((total_kv + Q) / ideal) (its N is at most total_kv + Q,
+  // its chunk length at least ideal). Launching no workgroup beyond these
+  // bounds matters because a surplus workgroup only gets a compute unit once
+  // a working one has finished, and then adds its own start-up to the end of
+  // the launch.
   int64_t live = max_chunks;
-  if (B == 1) live = std::min<int64_t>((total_kv + Q + ideal - 1) / ideal, max_chunks);
+  if (B == 1) live = std::min<int64_t>(live, (total_kv + Q + ideal - 1) / ideal);
+  if (p->target > B && B <= va::kPlanThreads) live = std::min<int64_t>(live, p->target);
   const int64_t grid = (live + 7) / 8 * 8 * p->row_tiles;
   if (grid > INT32_MAX) return false;
   p->grid = (int32_t)grid;

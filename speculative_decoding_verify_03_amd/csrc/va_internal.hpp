@@ -15,6 +15,8 @@ constexpr int kRowsPerBlock = 32;      // query-head rows of one 32x32 MFMA scor
 constexpr int kRowBlocksPerWG = 4;     // score blocks per workgroup (one per wave pair)
 constexpr int kRowsPerWG = kRowsPerBlock * kRowBlocksPerWG;  // 128 rows per row tile
 constexpr int kMinChunk = 128;         // smallest chunk worth a workgroup (keys): four tiles
+constexpr int kPlanThreads = 512;      // threads of the split workgroup, which plans the chunks: the
+                                       // length search runs for batches of at most this many sequences
 
 // Host-side split plan (the split kernel picks the chunk length from the
 // sequence lengths: the shortest one, not below ideal_keys, that needs at

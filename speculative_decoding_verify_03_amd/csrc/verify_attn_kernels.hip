@@ -234,7 +234,6 @@ __device__ __forceinline__ void bf16x4_to_f16(u32x2 v, f16x8& dst, int base) {
 // ceil(N_b / L), N_b = clamped prefix + Q; its positions start at the running
 // sum of N.
 // ---------------------------------------------------------------------------
-constexpr int kPlanThreads = 512;   // the split kernel's workgroup size
 
 struct ChunkPlan {
   int64_t L;       // keys per chunk

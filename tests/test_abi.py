@@ -80,15 +80,22 @@ def test_bad_arguments_rejected_before_launch(lib, over, code):
 
 def test_plan_grid_covers_every_chunk(lib):
     """The grid gives row_tiles workgroups to every chunk the device plan can
-    produce, rounded up to groups of 8 chunks: for one sequence
-    ceil((total_kv + Q) / chunk_keys) chunks (its N is at most total_kv + Q and its
-    chunk length at least chunk_keys), for a batch the partial buffers' capacity."""
+    produce, rounded up to groups of 8 chunks: at most the partial buffers'
+    capacity; for one sequence at most ceil((total_kv + Q) / chunk_keys) (its N is
+    at most total_kv + Q and its chunk length at least chunk_keys); and, when the
+    plan searches a chunk length (a budget of CUs / row_tiles chunks above B), at
+    most that budget."""
     for B, Q, H, T, ck in [(1, 16, 64, 185016, 0), (1, 16, 8, 185016, 0), (1, 16, 64, 4112, 0),
-                           (1, 8, 16, 3008, 32), (1, 4, 8, 260, 0), (8, 8, 64, 528448, 0), (3, 4, 40, 6512, 32)]:
+                           (1, 8, 16, 3008, 32), (1, 4, 8, 260, 0), (8, 8, 64, 528448, 0), (3, 4, 40, 6512, 32),
+                           (600, 4, 8, 700000, 0)]:
         p = va.query_plan(B, Q, H, T, chunk_keys=ck)
         L = p["chunk_keys"]
-        need = -(-(T + Q) // L) if B == 1 else p["max_chunks"]
-        assert need <= p["max_chunks"]
+        need = p["max_chunks"]
+        if B == 1:
+            need = min(need, -(-(T + Q) // L))
+        budget = 256 // p["row_tiles"] if ck == 0 else 0   # 256 CUs: MI355X, and the plan's value without a device
+        if budget > B:
+            need = min(need, budget)
         assert p["grid"] == -(-need // 8) * 8 * p["row_tiles"], (B, Q, H, T, ck, p)
 
 
