@@ -90,6 +90,15 @@ def test_many_small_chunks_cross_the_tail(env):
         _check(env, w, label=f"chunk{chunk}", chunk_keys=chunk)
 
 
+def test_chunk_ending_where_the_tail_starts(env):
+    """Chunk lengths that divide the prefix, so that a chunk ends exactly where the
+    speculative tail starts: that chunk must not need the tail mask (it loads it
+    only when it reaches the tail), and the next one holds the whole tail."""
+    w = make_workload("tailedge", [310], B=2, Q=8, H=16, prefix_lens=[1024, 512], mask="tree", num_slots=2000)
+    for chunk in (32, 256, 512):
+        _check(env, w, label=f"tailedge{chunk}", chunk_keys=chunk)
+
+
 def test_many_chunks_per_sequence_slice_merge(env):
     """32-key chunks over ragged sequences give at least 64 chunks per sequence on
     average, so the merge runs in its slice form (one workgroup per row and 64-dim
