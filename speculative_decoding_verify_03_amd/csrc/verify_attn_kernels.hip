@@ -88,6 +88,12 @@ static_assert(kGatherWaves == kKeyGroups, "one gather wave per key group");
 
 __host__ __device__ constexpr int gather_kg(int j, int k) { return j + 0 * k; }
 __host__ __device__ constexpr int gather_line(int j, int k) { return k + 0 * j; }
+__host__ __device__ constexpr bool gather_lines_in_order() {
+  for (int j = 0; j < kKeyGroups; ++j)
+    for (int k = 0; k < kGatherLoads; ++k)
+      if (gather_line(j, k) != k) return false;
+  return kGatherLoads == 9;
+}
 // Line of a tile whose value operands wave w reads (its 64 value dims are
 // chunks 8w .. 8w + 7; see value_chunk).
 __host__ __device__ constexpr int value_line(int w) { return w; }
@@ -161,11 +167,26 @@ __device__ __forceinline__ GatherLane gather_lane(int gw, int lane) {
 // the load. The loads write LDS only, so no register is left pending; their
 // completion is awaited with explicit vmcnt waits, and the compiler's own
 // vmcnt waits only grow stricter for not counting them.
-__device__ __forceinline__ void lds_dma16_nt(const char* gaddr, LDS_AS char* lds_dst) {
+// The nine lines of one key group in one block: line L reads gaddr + 128 L
+// into lds_dst + 1024 L. The instruction offset (128 L) is added to the
+// global and to the LDS address alike, so M0 advances by 1024 - 128 per line
+// and the lane's address register serves all nine loads. (An SALU write of M0
+// needs one wait state before an LDS DMA reads it: the s_nop after each.)
+__device__ __forceinline__ void lds_dma16_nt_lines9(const char* gaddr, LDS_AS char* lds_dst) {
   const unsigned lb = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_dst);
   unsigned saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved) : "v"(gaddr), "s"(lb) : "memory");
+  asm volatile("s_mov_b32 %0, m0\n\t"
+               "s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt\n\t"
+               "s_add_u32 m0, m0, 0x380\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:128 nt\n\t"
+               "s_add_u32 m0, m0, 0x380\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:256 nt\n\t"
+               "s_add_u32 m0, m0, 0x380\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:384 nt\n\t"
+               "s_add_u32 m0, m0, 0x380\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:512 nt\n\t"
+               "s_add_u32 m0, m0, 0x380\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:640 nt\n\t"
+               "s_add_u32 m0, m0, 0x380\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:768 nt\n\t"
+               "s_add_u32 m0, m0, 0x380\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:896 nt\n\t"
+               "s_add_u32 m0, m0, 0x380\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:1024 nt\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(gaddr), "s"(lb) : "memory", "scc");
 }
 __device__ __forceinline__ void lds_dma4(const void* gaddr, LDS_AS char* lds_dst) {
   const unsigned lb = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_dst);
@@ -185,11 +206,8 @@ __device__ __forceinline__ void issue_tile_gather(const char* kv_pool, int64_t n
   const char* row = (slot >= 0 && slot < num_slots) ? kv_pool + (int64_t)slot * kRowBytes
                                                     : reinterpret_cast<const char*>(g_zero_row);
   row += gl.coff;
-#pragma unroll
-  for (int k = 0; k < kGatherLoads; ++k) {
-    const int L = gather_line(gl.kg, k);
-    lds_dma16_nt(row + L * 128, tile + (gl.kg * 9 + L) * 1024);
-  }
+  static_assert(gather_lines_in_order(), "lds_dma16_nt_lines9 issues lines 0..8 in order");
+  lds_dma16_nt_lines9(row, tile + gl.kg * 9 * 1024);
 }
 
 __device__ __forceinline__ LDS_AS char* lds_cast(char* p) { return (LDS_AS char*)(p); }
