@@ -274,25 +274,26 @@ def bench_tree_accept(args, torch, va) -> int:
 def summarize_trace(path: str, config: str, warmup: int, steps: int) -> str:
     """Markdown summary of a rocprofv3 kernel-trace CSV of `bench.py --config config
     --warmup W --steps K`: the split and merge kernels of the timed calls only. The run
-    makes W warmup calls, then K steps of four calls (cold call, cold split-kernel
-    timing, warm call, warm split-kernel timing); each call is one split and one merge
-    dispatch, in that order."""
+    makes W warmup steps, then K timed steps, each of four calls (cold call, cold
+    split-kernel timing, warm call, warm split-kernel timing); each call is one split
+    and one merge dispatch, in that order."""
     import csv
     rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
     split = [r for r in rows if "split_kernel" in r["Kernel_Name"]]
     merge = [r for r in rows if "merge" in r["Kernel_Name"] and "va" in r["Kernel_Name"]]
-    n = warmup + 4 * steps
+    first = 4 * warmup   # calls of the warmup steps
+    n = first + 4 * steps
     if len(split) != n or len(merge) != n:
         raise SystemExit(f"expected {n} split and merge dispatches, found {len(split)} and {len(merge)}")
     dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3  # noqa: E731
     kinds = {"cold": (0, 1), "warm": (2, 3)}
     w = None
-    out = [f"Timed calls only: the first {warmup} calls (warmup) are dropped; {steps} steps of four calls "
+    out = [f"Timed calls only: the first {first} calls ({warmup} warmup steps) are dropped; {steps} steps of four calls "
            "remain (cold call, cold split-kernel timing, warm call, warm split-kernel timing).", "",
            "| kernel | calls | kind | avg us | min us | max us |", "|---|---:|---|---:|---:|---:|"]
     stats = {}
     for kind, idx in kinds.items():
-        sel = [warmup + 4 * k + i for k in range(steps) for i in idx]
+        sel = [first + 4 * k + i for k in range(steps) for i in idx]
         for name, lst in (("split_kernel", split), (merge[0]["Kernel_Name"].split("(")[0], merge)):
             d = np.array([dur(lst[i]) for i in sel])
             stats[(name, kind)] = d
@@ -390,11 +391,6 @@ def main() -> int:
         va.verify_attn(q, kv, idx, pl, tm, scale, out=out, lse=lse, workspace=ws, chunk_keys=args.chunk,
                        split_events=split_events)
 
-    print(f"[bench] plan {plan}; warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
-
     def timed(n, do_flush):
         """n timed steps. Each step makes four calls, so that any drift of the
         GPU's clocks during the run affects every figure alike: a cold call (after
@@ -425,6 +421,12 @@ def main() -> int:
         t = lambda i: np.array([x[i].elapsed_time(x[i + 1]) for x in ev]) * 1e3  # noqa: E731
         return t(0), t(2), t(4), t(6), wall
 
+    # Warmup steps run the timed pattern, evictions included: the 1 GiB reads
+    # change the GPU's power state, and its clocks take tens of calls to
+    # settle after they start (a warmup of plain calls left the first timed
+    # calls up to 25% slower than the later ones).
+    print(f"[bench] plan {plan}; warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    timed(args.warmup, flush is not None)
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     calls, splits, warm_calls, warm_splits, wall = timed(args.steps, flush is not None)
 
