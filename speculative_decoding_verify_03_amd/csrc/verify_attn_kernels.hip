@@ -979,6 +979,16 @@ split_kernel(SplitArgs a) {
   }
 }
 
+// Chunk range [c0, c1) of sequence b for the merges, clamped to the partial
+// buffers' capacity. The split kernel writes offsets inside it; the clamp keeps
+// every partial read in bounds whatever the offsets hold.
+__device__ __forceinline__ int2 chunk_range(const int32_t* __restrict__ chunk_off, int b, int max_chunks) {
+  int c0 = chunk_off[b], c1 = chunk_off[b + 1];
+  c0 = c0 < 0 ? 0 : (c0 > max_chunks ? max_chunks : c0);
+  c1 = c1 < c0 ? c0 : (c1 > max_chunks ? max_chunks : c1);
+  return int2{c0, c1};
+}
+
 // ---------------------------------------------------------------------------
 // Merge: lse = ln sum_s exp(lse_s); out = sum_s exp(lse_s - lse) O_s.
 // One 256-thread workgroup per (row, quarter of the 512 value dims): thread
@@ -996,7 +1006,7 @@ __global__ void __launch_bounds__(256) merge_kernel(const _Float16* __restrict__
                                                     const float* __restrict__ part_lse,
                                                     const int32_t* __restrict__ chunk_off,
                                                     float* __restrict__ out, float* __restrict__ lse,
-                                                    int B, int R) {
+                                                    int B, int R, int max_chunks) {
   __shared__ f32x4 s_acc[kMergeLanes][32];
   __shared__ float s_m[kMergeLanes];
   __shared__ float s_w[kMergeLanes];
@@ -1007,7 +1017,8 @@ __global__ void __launch_bounds__(256) merge_kernel(const _Float16* __restrict__
   const int r = (int)(grow - (int64_t)b * R);
   const int t = threadIdx.x;
   const int dl = t & 31, cl = t >> 5;
-  const int c0 = chunk_off[b], c1 = chunk_off[b + 1];
+  const int2 cr = chunk_range(chunk_off, b, max_chunks);
+  const int c0 = cr.x, c1 = cr.y;
   float* orow = out + grow * kValue + qd * 128 + 4 * dl;
   if (c1 <= c0) {   // no chunk (only when the partial buffers ran out)
     if (cl == 0) *reinterpret_cast<f32x4*>(orow) = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1107,7 +1118,7 @@ __global__ void __launch_bounds__(256) merge_slice_kernel(const _Float16* __rest
                                                           const float* __restrict__ part_lse,
                                                           const int32_t* __restrict__ chunk_off,
                                                           float* __restrict__ out, float* __restrict__ lse,
-                                                          int B, int R) {
+                                                          int B, int R, int max_chunks) {
   __shared__ float s_acc[kSliceLanes][64];
   __shared__ float s_m[kSliceLanes];
   __shared__ float s_w[kSliceLanes];
@@ -1118,7 +1129,8 @@ __global__ void __launch_bounds__(256) merge_slice_kernel(const _Float16* __rest
   const int r = (int)(grow - (int64_t)b * R);
   const int t = threadIdx.x;
   const int dl = t & 7, cl = t >> 3;
-  const int c0 = chunk_off[b], c1 = chunk_off[b + 1];
+  const int2 cr = chunk_range(chunk_off, b, max_chunks);
+  const int c0 = cr.x, c1 = cr.y;
   const _Float16* obase = part_o + (int64_t)r * kValue + slice * 64 + dl * 8;
   float m = -INFINITY, ws = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -1197,7 +1209,7 @@ __global__ void __launch_bounds__(256) merge_few_kernel(const _Float16* __restri
                                                         const float* __restrict__ part_lse,
                                                         const int32_t* __restrict__ chunk_off,
                                                         float* __restrict__ out, float* __restrict__ lse,
-                                                        int B, int R) {
+                                                        int B, int R, int max_chunks) {
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (row, half)
   if (item >= (int64_t)B * R * 2) return;   // uniform per wave
@@ -1205,7 +1217,8 @@ __global__ void __launch_bounds__(256) merge_few_kernel(const _Float16* __restri
   const int half = (int)(item & 1);
   const int b = (int)(grow / R);
   const int r = (int)(grow - (int64_t)b * R);
-  const int c0 = chunk_off[b], c1 = chunk_off[b + 1];
+  const int2 cr = chunk_range(chunk_off, b, max_chunks);
+  const int c0 = cr.x, c1 = cr.y;
   float* orow = out + grow * kValue + half * 256 + 4 * lane;
   const _Float16* obase = part_o + (int64_t)r * kValue + half * 256 + 4 * lane;
   float m = -INFINITY, ws = 0.f;
@@ -1329,13 +1342,13 @@ hipError_t launch_merge(const _Float16* part_o, const float* part_lse, const int
   const int64_t rows = (int64_t)B * R;
   if (max_chunks <= kMergeFewPerSeq * B) {   // few chunks per sequence on average
     hipLaunchKernelGGL(merge_few_kernel, dim3((unsigned)((rows * 2 + 3) / 4)), dim3(256), 0, stream, part_o,
-                       part_lse, chunk_off, out, lse, B, R);
+                       part_lse, chunk_off, out, lse, B, R, max_chunks);
   } else if (max_chunks >= kMergeSlicePerSeq * B) {   // many chunks per sequence
     hipLaunchKernelGGL(merge_slice_kernel, dim3((unsigned)(rows * kSlices)), dim3(256), 0, stream, part_o,
-                       part_lse, chunk_off, out, lse, B, R);
+                       part_lse, chunk_off, out, lse, B, R, max_chunks);
   } else {
     hipLaunchKernelGGL(merge_kernel, dim3((unsigned)(rows * 4)), dim3(256), 0, stream, part_o,
-                       part_lse, chunk_off, out, lse, B, R);
+                       part_lse, chunk_off, out, lse, B, R, max_chunks);
   }
   return hipGetLastError();
 }
