@@ -65,12 +65,13 @@ bool dims_ok(int B, int Q, int H, int64_t total_kv) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// The split plan. Workgroups are (chunk, 128-row tile) pairs and one
+// The split plan. Workgroups are (column, 128-row tile) pairs and one
 // workgroup fills a compute unit (8 waves, ~159 KiB of LDS), so the batch
-// gets a budget of floor(CUs / row_tiles) chunks; the split kernel then picks
-// the shortest chunk length (at least total_kv / budget) whose chunks fit in
-// the budget. A forced chunk length (chunk_keys > 0, tests and tuning only)
-// is used as is.
+// gets a budget of floor(CUs / row_tiles) columns. With fewer sequences than
+// that (and at most kPlanThreads) the split kernel cuts the batch's key tiles
+// into at most that many equal columns, one piece per sequence a column
+// meets; otherwise, and with a forced chunk length (chunk_keys > 0, tests and
+// tuning only), every column is one chunk of ideal_keys keys.
 bool make_plan(int B, int Q, int H, int64_t total_kv, int ncu, int32_t chunk_keys, va::Plan* p) {
   if (!dims_ok(B, Q, H, total_kv)) return false;
   const int64_t R = (int64_t)Q * H;
@@ -84,21 +85,21 @@ bool make_plan(int B, int Q, int H, int64_t total_kv, int ncu, int32_t chunk_key
   ideal = (ideal + va::kUnit - 1) / va::kUnit * va::kUnit;
   p->target = ov > 0 ? 0 : (int32_t)target;   // a forced length is used as is
   p->ideal_keys = (int32_t)ideal;
-  // The chunk length is at least ideal and a sequence of N_b keys takes
-  // ceil(N_b / length) chunks, so the batch never needs more than
-  // total_kv / ideal + B of them.
+  // Partial buffers: a sequence of N_b keys takes ceil(N_b / ideal) chunks,
+  // so the chunk plan never needs more than total_kv / ideal + B of them; the
+  // column plan uses at most max_chunks - B + 1 columns, and so at most
+  // max_chunks pieces.
   const int64_t max_chunks = total_kv / ideal + B + 1;
   if (max_chunks > INT32_MAX / 8) return false;
   p->max_chunks = (int32_t)max_chunks;
-  // Workgroups: the row tiles of every chunk the kernel's plan can produce,
-  // rounded up to whole groups of 8 chunks (the XCD mapping). When the plan
-  // searches a chunk length (a budget above B, at most kPlanThreads
-  // sequences) it produces at most `target` chunks; a batch of one sequence
-  // has at most ceil((total_kv + Q) / ideal) (its N is at most total_kv + Q,
-  // its chunk length at least ideal). Launching no workgroup beyond these
-  // bounds matters because a surplus workgroup only gets a compute unit once
-  // a working one has finished, and then adds its own start-up to the end of
-  // the launch.
+  // Workgroups: the row tiles of every column, rounded up to whole groups of
+  // 8 columns (the XCD mapping). The column plan (a budget above B, at most
+  // kPlanThreads sequences) uses at most `target` columns, and no more than
+  // are launched; a batch of one sequence is given at most
+  // ceil((total_kv + Q) / ideal) of them (pieces of about ideal keys).
+  // Launching no workgroup beyond these bounds matters because a surplus
+  // workgroup only gets a compute unit once a working one has finished, and
+  // then adds its own start-up to the end of the launch.
   int64_t live = max_chunks;
   if (B == 1) live = std::min<int64_t>(live, (total_kv + Q + ideal - 1) / ideal);
   if (p->target > B && B <= va::kPlanThreads) live = std::min<int64_t>(live, p->target);

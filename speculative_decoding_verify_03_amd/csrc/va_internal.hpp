@@ -15,17 +15,17 @@ constexpr int kRowsPerBlock = 32;      // query-head rows of one 32x32 MFMA scor
 constexpr int kRowBlocksPerWG = 4;     // score blocks per workgroup (one per wave pair)
 constexpr int kRowsPerWG = kRowsPerBlock * kRowBlocksPerWG;  // 128 rows per row tile
 constexpr int kMinChunk = 128;         // smallest chunk worth a workgroup (keys): four tiles
-constexpr int kPlanThreads = 512;      // threads of the split workgroup, which plans the chunks: the
-                                       // length search runs for batches of at most this many sequences
+constexpr int kPlanThreads = 512;      // threads of the split workgroup, which plans the pieces: the
+                                       // column plan runs for batches of at most this many sequences
 
-// Host-side split plan (the split kernel picks the chunk length from the
-// sequence lengths: the shortest one, not below ideal_keys, that needs at
-// most `target` chunks).
+// Host-side split plan (the split kernel plans the pieces from the sequence
+// lengths: equal columns of the batch's key tiles, at most `target` of them,
+// when there are fewer sequences than that, else chunks of ideal_keys keys).
 struct Plan {
   int32_t row_tiles;    // ceil(Q*H / 128)
-  int32_t target;       // chunk budget over the whole batch; 0 = use ideal_keys as is
-  int32_t ideal_keys;   // keys per chunk that would hit `target` exactly (multiple of 32)
-  int32_t max_chunks;   // capacity of the partial buffers (chunks)
+  int32_t target;       // column budget over the whole batch; 0 = chunks of ideal_keys as is
+  int32_t ideal_keys;   // keys per column that would hit `target` exactly (multiple of 32)
+  int32_t max_chunks;   // capacity of the partial buffers (pieces)
   int32_t grid;         // split-kernel workgroups
   size_t off_chunk;     // workspace byte offsets
 
@@ -40,7 +40,7 @@ struct SplitArgs {
   const int32_t* kv_indices;
   const int32_t* prefix_lens;
   const uint8_t* tree_mask;
-  int32_t* chunk_off;      // written by workgroup 0: [B + 1] chunk offsets for the merge
+  int32_t* chunk_off;      // written by workgroup 0: [B + 1] piece offsets for the merge
   _Float16* part_o;       // [max_chunks][R][512] fp16, normalised (O / l)
   float* part_lse;
   int64_t num_slots;

@@ -4,10 +4,11 @@
 // Context: A Custom Kernel for an Unsupported Architecture"; page "The Build
 // That Bridged Design and Deployment: Compiling the Custom sm_120 Verify
 // Kernel", section "What This Build Achieves: The paged+bf16 Kernel"):
-// flash-decode. The KV positions of each sequence are cut into
-// chunks; every (chunk, 128-row tile) pair is one workgroup that streams its
-// chunk through LDS in 32-key tiles with an online softmax, and a second
-// kernel merges the chunk partials by log-sum-exp.
+// flash-decode. The KV positions of the batch are cut into pieces (whole
+// columns of the batch's key tiles, one piece per sequence a column meets);
+// every (column, 128-row tile) pair is one workgroup that streams its pieces
+// through LDS in 32-key tiles with an online softmax, leaving one partial per
+// piece, and a second kernel merges each sequence's partials by log-sum-exp.
 //
 // gfx950 mapping, per workgroup (8 waves, two per SIMD, 128 query-head rows):
 //  * gather: every 32-key tile is brought into LDS with 16-byte direct
@@ -26,8 +27,8 @@
 //    same LDS tile with the gfx950 transpose read ds_read_b64_tr_b16 and
 //    converted bf16 -> fp16 in registers. P is fp16 (not bf16) for accuracy:
 //    fp16 keeps 11 significant bits against bf16's 8;
-//  * partials: each chunk leaves O / l in fp16 (bounded by the largest |value|
-//    of the chunk) and its lse in fp32; the merge folds them in fp32.
+//  * partials: each piece leaves O / l in fp16 (bounded by the largest |value|
+//    of the piece) and its lse in fp32; the merge folds them in fp32.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -214,11 +215,22 @@ __device__ __forceinline__ LDS_AS char* lds_cast(char* p) { return (LDS_AS char*
 
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
+// x of lane l ^ 32 (the other half of the wave); `addr` = 4 (l ^ 32).
+__device__ __forceinline__ float swap_halves(float x, int addr) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(x)));
+}
+
 
 // The lane id, re-derived where it is used: as a volatile asm result it cannot
 // be hoisted out of a loop, so per-lane addresses built from it are
 // recomputed in place instead of occupying registers across the loop.
+// A wave-uniform 64-bit value, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ int fresh_lane() {
   int l;
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
@@ -241,25 +253,41 @@ __device__ __forceinline__ void bf16x4_to_f16(u32x2 v, f16x8& dst, int base) {
 }
 
 // ---------------------------------------------------------------------------
-// Chunk plan, computed by every split workgroup at its start (identically, from
-// prefix_lens alone): one chunk length L for the batch, and where chunk c sits.
-// Every chunk but a sequence's last holds exactly L keys, so L is the split
-// kernel's critical path. With a chunk budget (target > 0) L is the smallest
-// multiple of 32 keys, not below ideal_keys, for which the batch needs at
-// most `target` chunks; without one (target == 0), or when the batch has at
-// least `target` (or more than 512) sequences, L = ideal_keys. Sequence b owns
-// chunks [chunk_off[b], chunk_off[b+1]) with chunk_off the running sum of
-// ceil(N_b / L), N_b = clamped prefix + Q; its positions start at the running
-// sum of N.
+// Split plans, computed by every split workgroup at its start (identically,
+// from prefix_lens alone). Sequence b has N_b = clamped prefix + Q keys, and
+// its positions start at the running sum of N. Under either plan it owns the
+// partials [chunk_off[b], chunk_off[b+1]), which workgroup 0 writes for the
+// merge.
+//
+// Column plan (a chunk budget, target > 0, above the number of sequences, and
+// at most 512 sequences): the batch's 32-key tiles are laid end to end,
+// sequence after sequence, each sequence's tiles preceded by kSeqUnits units
+// that stand for what starting a piece costs (a prologue and an epilogue),
+// and this axis is cut into columns of ceil(U / C) units (U the axis length,
+// C = min(target, max_chunks - B + 1, launched columns)), one per workgroup
+// of each row tile. A column runs one piece per sequence whose tiles it
+// meets, so the workgroups end within about a tile of each other whatever the
+// sequences' lengths. There are at most C + B - 1 pieces, which the partial
+// buffers hold.
+//
+// Chunk plan (otherwise): one chunk length L = ideal_keys for the batch;
+// sequence b owns ceil(N_b / L) chunks, and chunk c is workgroup c's piece.
 // ---------------------------------------------------------------------------
 
+// What one workgroup (one column of row tiles) does: nseg pieces, each a key
+// range of one sequence with a partial of its own. The first piece is given in
+// full; under the column plan (below) the next one, if any, is always the next
+// sequence from its first key, with partial index c + 1.
 struct ChunkPlan {
-  int64_t L;       // keys per chunk
-  int64_t sbase;   // first position of the chunk's sequence
-  int64_t P;       // its clamped prefix length
-  int32_t b;       // its sequence
-  int32_t coff;    // its first chunk
-  int32_t total;   // chunks of the batch (capped at max_chunks)
+  int64_t sbase;    // first position of the first piece's sequence
+  int64_t P;        // its clamped prefix length
+  int64_t kstart;   // the piece's keys [kstart, kend) within its sequence
+  int64_t kend;
+  int64_t ubase;    // column plan: axis unit where that sequence's tiles start
+  int64_t uend;     // column plan: axis unit where the column ends
+  int32_t b;        // the piece's sequence
+  int32_t c;        // its partial index
+  int32_t nseg;     // pieces of this workgroup (0: nothing to do)
 };
 
 // Sum over the kPlanThreads threads of the workgroup; every thread gets the total.
@@ -304,26 +332,7 @@ __device__ ChunkPlan chunk_plan(const SplitArgs& a, int c, bool write_offsets, L
   };
   if (tid == 0) own[0] = -1;
 
-  int64_t L = a.ideal_keys;
-  if (a.target > B && B <= kPlanThreads) {
-    // Thread b holds N_b. Chunks needed at length `len`: the sum of
-    // ceil(N_b / len), at most sum N_b / len + B, so lengths from
-    // sum N_b / (target - B) on fit.
-    const int64_t mine = tid < B ? keys_of(tid) : 0;
-    auto count = [&](int64_t len) -> int64_t { return block_sum((mine + len - 1) / len, red); };
-    int64_t lo = a.ideal_keys / kUnit;
-    if (count(lo * kUnit) > a.target) {   // uniform across the workgroup
-      const int64_t nsum = block_sum(mine, red);
-      int64_t hi = (nsum / (a.target - B) + kUnit) / kUnit;
-      if (hi <= lo) hi = lo + 1;
-      ++lo;   // lo itself does not fit
-      while (lo < hi) {
-        const int64_t mid = (lo + hi) >> 1;
-        if (count(mid * kUnit) <= a.target) hi = mid; else lo = mid + 1;
-      }
-    }
-    L = lo * kUnit;
-  }
+  const int64_t L = a.ideal_keys;
 
   // Running sums over the batch, kPlanThreads sequences per pass.
   int64_t carry_n = 0;
@@ -366,17 +375,147 @@ __device__ ChunkPlan chunk_plan(const SplitArgs& a, int c, bool write_offsets, L
   if (write_offsets && tid == 0) a.chunk_off[B] = carry_c < a.max_chunks ? carry_c : a.max_chunks;
   __syncthreads();
   ChunkPlan cp;
-  cp.L = L;
-  cp.total = carry_c < a.max_chunks ? carry_c : a.max_chunks;
+  const int32_t total = carry_c < a.max_chunks ? carry_c : a.max_chunks;
   cp.b = (int32_t)own[0];
-  cp.coff = (int32_t)own[1];
+  cp.c = c;
+  cp.nseg = c < total ? 1 : 0;
   cp.sbase = own[2];
   cp.P = own[3];
+  cp.kstart = (int64_t)(c - (int32_t)own[1]) * L;
+  cp.kend = cp.kstart + L;
+  cp.ubase = cp.uend = 0;
+  return cp;
+}
+
+// Axis units that stand for starting a piece: about what a second prologue and
+// epilogue cost a workgroup, in 32-key tiles of its loop.
+constexpr int kSeqUnits = 3;
+
+// Inclusive prefix sum over the 64 lanes of a wave through DPP moves (no LDS
+// round trips): three shifts by 1-3 lanes and two by 4 and 8 within each row
+// of 16 lanes, then the broadcasts of lanes 15 and 31 into the rows after
+// them. Lanes a move does not reach take 0.
+__device__ __forceinline__ int32_t wave_scan_dpp(int32_t x) {
+  int32_t s = x;
+  s += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  s += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  s += __builtin_amdgcn_update_dpp(0, x, 0x113, 0xf, 0xf, false);   // row_shr:3
+  s += __builtin_amdgcn_update_dpp(0, s, 0x114, 0xf, 0xe, false);   // row_shr:4, lanes 4-15 of a row
+  s += __builtin_amdgcn_update_dpp(0, s, 0x118, 0xf, 0xc, false);   // row_shr:8, lanes 8-15 of a row
+  s += __builtin_amdgcn_update_dpp(0, s, 0x142, 0xa, 0xf, false);   // row_bcast:15, rows 1 and 3
+  s += __builtin_amdgcn_update_dpp(0, s, 0x143, 0xc, 0xf, false);   // row_bcast:31, rows 2 and 3
+  return s;
+}
+
+// The column plan for column g (see above). All kPlanThreads threads call it
+// with the same g; `scratch` is 512 bytes of LDS that nothing else uses until
+// the workgroup's next barrier after the call. Requires 0 < B <= kPlanThreads
+// and target > B. Running sums of keys and axis units are 64-bit (prefix
+// lengths need not add up to total_kv); a column's units and its pieces fit
+// in 32 bits.
+__device__ ChunkPlan column_plan(const SplitArgs& a, int g, bool write_offsets, LDS_AS char* scratch) {
+  LDS_AS int64_t* wu = reinterpret_cast<LDS_AS int64_t*>(scratch);   // 8 wave totals of units
+  LDS_AS int64_t* wn = wu + 8;                                       // 8 wave totals of keys
+  LDS_AS int32_t* wp = reinterpret_cast<LDS_AS int32_t*>(wu + 16);   // 8 wave totals of pieces
+  LDS_AS int32_t* wm = wp + 8;                                       // 8 wave counts of pieces of column g
+  LDS_AS int64_t* own = wu + 24;                                     // the column's first piece
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int B = a.B;
+  const bool mine = tid < B;   // thread b holds sequence b
+  int64_t nb = 0;
+  if (mine) {
+    int64_t pl = a.prefix_lens[tid];
+    pl = pl < 0 ? 0 : (pl > a.total_kv ? a.total_kv : pl);
+    nb = pl + a.Q;
+  }
+  const int64_t tb = (nb + kUnit - 1) / kUnit;   // tiles
+  const int64_t ub = mine ? kSeqUnits + tb : 0;   // axis units
+
+  // Inclusive scans of units and keys over the batch (one pass: B <= 512).
+  int64_t in_u = wave_scan(ub, lane);
+  int64_t in_n = wave_scan(nb, lane);
+  if (tid == 0) own[0] = -1;
+  if (lane == 63) {
+    wu[wave] = in_u;
+    wn[wave] = in_n;
+  }
+  __syncthreads();
+  int64_t U = 0;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    if (w < wave) {
+      in_u += wu[w];
+      in_n += wn[w];
+    }
+    U += wu[w];
+  }
+  const int64_t ta = in_u - tb;   // first tile unit of sequence tid; its tiles end at in_u
+  const int64_t sb = in_n - nb;   // its first position
+
+  // Columns: column j covers units [j W, min((j + 1) W, U)) with W =
+  // ceil(U / C), so unit x lies in column x / W.
+  int C = a.max_chunks - B + 1;                     // pieces fit the partial buffers
+  if (C > a.target) C = a.target;                   // one wave of workgroups
+  const int launched = (int)(gridDim.x / a.row_tiles);
+  if (C > launched) C = launched;                   // every column has its workgroups
+  if (C < 1) C = 1;
+  const int64_t W = (U + C - 1) / C;                // uniform: one division
+  const bool small = U < ((int64_t)1 << 31);        // always, when the lengths fit the array
+  auto col = [&](int64_t x) -> int32_t {
+    return small ? (int32_t)((uint32_t)x / (uint32_t)W) : (int32_t)(x / W);
+  };
+  const int32_t cs = mine ? col(ta) : 0;
+  const int32_t ce = mine ? col(in_u - 1) : -1;
+  const int32_t np = ce - cs + 1;   // pieces of sequence tid (0 for no sequence)
+  // The column's pieces: the sequences whose tiles meet it, which are
+  // consecutive; the first is the one whose predecessor's tiles end before it.
+  const bool meets = mine && cs <= g && g <= ce;
+  int32_t in_p = wave_scan_dpp(np);
+  const int32_t wave_meets = (int32_t)__builtin_popcountll(__ballot(meets));   // all lanes take part
+  if (lane == 63) wp[wave] = in_p;
+  if (lane == 0) wm[wave] = wave_meets;
+  __syncthreads();
+  int32_t total = 0, nseg = 0;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    if (w < wave) in_p += wp[w];
+    total += wp[w];
+    nseg += wm[w];
+  }
+  const int32_t off = in_p - np;
+  if (write_offsets && mine) a.chunk_off[tid] = off < a.max_chunks ? off : a.max_chunks;
+  if (write_offsets && tid == 0) a.chunk_off[B] = total < a.max_chunks ? total : a.max_chunks;
+
+  const bool first = meets && (tid == 0 || col(ta - kSeqUnits - 1) < g);
+  if (first) {
+    own[0] = tid;
+    own[1] = off + (g - cs);
+    own[2] = sb;
+    own[3] = nb - a.Q;
+    own[4] = ta;
+  }
+  __syncthreads();
+  ChunkPlan cp;
+  cp.b = (int32_t)own[0];
+  cp.c = (int32_t)own[1];
+  cp.sbase = own[2];
+  cp.P = own[3];
+  cp.ubase = own[4];
+  const int64_t lo = (int64_t)g * W;
+  cp.uend = lo + W < U ? lo + W : U;
+  cp.kstart = ((lo > cp.ubase ? lo : cp.ubase) - cp.ubase) * kUnit;
+  cp.kend = (cp.uend - cp.ubase) * kUnit;
+  // Bounds that hold by construction, kept so that no piece can index past
+  // the sequences or the partial buffers.
+  int32_t ns = cp.b < 0 ? 0 : nseg;
+  if (cp.b + ns > B) ns = B - cp.b;
+  if (cp.c + ns > a.max_chunks) ns = a.max_chunks - cp.c;
+  cp.nseg = ns > 0 ? ns : 0;
   return cp;
 }
 
 // ---------------------------------------------------------------------------
-// Split kernel: one workgroup per (chunk, 128-row tile).
+// Split kernel: one workgroup per (column, 128-row tile).
 //
 // 8 waves, two per SIMD. Waves j and j+4 (same SIMD) form pair j and own
 // query-head rows [32j, 32j + 32) of the tile for the scores: wave half
@@ -390,7 +529,7 @@ __device__ ChunkPlan chunk_plan(const SplitArgs& a, int c, bool write_offsets, L
 // ---------------------------------------------------------------------------
 constexpr int kSplitWaves = 8;
 constexpr int kSplitThreads = kSplitWaves * 64;
-static_assert(kSplitThreads == kPlanThreads, "the chunk plan runs on the split workgroup");
+static_assert(kSplitThreads == kPlanThreads, "the split plan runs on the split workgroup");
 constexpr int kRingS = 3;                               // tiles resident in LDS
 constexpr int kPairs = 4;
 constexpr int kHalfKSteps = kKSteps / 2;                // 18 k-steps per wave
@@ -410,7 +549,8 @@ constexpr int kSlotRing = 8;                                       // 256 bytes 
 constexpr int kGatherAhead = 3;                                    // tile u+3 is gathered while tile u is applied
 constexpr int kSlotAhead = 5;                                      // slot copy distance, tiles
 constexpr int kOffQPark = kOffSlots + kSlotRing * 256;             // 146496
-constexpr int kSplitLds = kOffQPark + kSplitWaves * kQParkBytes;   // 162880
+constexpr int kOffPlan = kOffQPark + kSplitWaves * kQParkBytes;    // 162880: the column's first piece
+constexpr int kSplitLds = kOffPlan + 64;                             // 162944
 static_assert(kSplitLds <= 160 * 1024, "split kernel LDS budget");
 // A slot copy issued in phase X of iteration v lands before the barrier that
 // ends phase X of iteration v+1; gathers read it kGatherAhead tiles ahead of
@@ -476,37 +616,53 @@ split_kernel(SplitArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int n = lane & 31;   // row of this lane within a 32-row block
-  const int h = lane >> 5;   // k-half of the MFMA operands
+  // Lane-derived values are re-derived from fresh_lane() for each piece (the
+  // loop over pieces below), so that nothing computed from them is hoisted out
+  // of that loop and kept live through all of it.
+  int lane = tid & 63;
+  int n = lane & 31;   // row of this lane within a 32-row block
+  int h = lane >> 5;   // k-half of the MFMA operands
+  int swap_addr = (lane ^ 32) << 2;   // LDS permute address of the lane in the other half
   const int pair = wave & 3;
   const int p = wave >> 2;   // 0: even half (softmax owner), 1: odd half
 
-  // Workgroup -> (chunk, row tile). Consecutive ids go round-robin to the 8
-  // XCDs, so all row tiles of one chunk share an XCD and its L2.
+  // Workgroup -> (column, row tile). Consecutive ids go round-robin to the 8
+  // XCDs, so all row tiles of one column share an XCD and its L2.
   const int wg = blockIdx.x;
   const int xcd = wg & 7;
   const int y = wg >> 3;
   const int rt = y % a.row_tiles;
-  const int c = (y / a.row_tiles) * 8 + xcd;
+  const int g = (y / a.row_tiles) * 8 + xcd;
   // (P region of LDS as scratch: first written by the softmax of tile 0,
   // after several barriers.)
-  const ChunkPlan cp = chunk_plan(a, c, wg == 0, lds + kOffP);
-  if (c >= cp.total) return;   // uniform across the workgroup
-  const int b = cp.b;
-  const int64_t P = cp.P;
-  const int64_t N = P + a.Q;
-  const int64_t sbase = cp.sbase;
-  const int64_t kstart = (int64_t)(c - cp.coff) * cp.L;
-  int64_t kend = kstart + cp.L;
-  if (kend > N) kend = N;
-  if (kend > a.total_kv - sbase) kend = a.total_kv - sbase;  // positions past the array are absent
-  const int nunits = kend > kstart ? (int)((kend - kstart + kUnit - 1) / kUnit) : 0;
+  const bool columns = a.target > a.B && a.B <= kPlanThreads;   // uniform across the launch
+  const ChunkPlan cp = columns ? column_plan(a, g, wg == 0, lds + kOffP) : chunk_plan(a, g, wg == 0, lds + kOffP);
+  if (cp.nseg == 0) return;   // uniform across the workgroup
+  // The first piece's description stays in LDS for the later pieces (read
+  // there, after the barriers of the first piece), so that it does not occupy
+  // registers through the loop over pieces.
+  LDS_AS int64_t* plan_st = reinterpret_cast<LDS_AS int64_t*>(lds + kOffPlan);
+  if (tid == 0) {
+    plan_st[0] = cp.b;
+    plan_st[1] = cp.c;
+    plan_st[2] = cp.sbase;
+    plan_st[3] = cp.ubase;
+    plan_st[4] = cp.uend;
+    plan_st[5] = cp.nseg;
+  }
+  // The current piece (see ChunkPlan); set for each piece below.
+  int b = __builtin_amdgcn_readfirstlane(cp.b);
+  int c = __builtin_amdgcn_readfirstlane(cp.c);
+  int64_t P = uniform64(cp.P);
+  int64_t sbase = uniform64(cp.sbase);
+  int64_t kstart = uniform64(cp.kstart);
+  int64_t kend = uniform64(cp.kend);
+  int nunits = 0;
 
   // Score rows of this lane (pair block) and its query's tail-visibility bits.
-  const int r = rt * kRowsPerWG + pair * 32 + n;
-  const bool row_ok = r < a.R;
-  const int rr = row_ok ? r : 0;
+  auto row_of_lane = [&]() { return rt * kRowsPerWG + pair * 32 + n; };
+  bool row_ok = row_of_lane() < a.R;
+  int rr = row_ok ? row_of_lane() : 0;
   // Tail-visibility bits of the lane's query (even half; all ones elsewhere).
   // The first 16 positions are 16 unconditional byte loads (indices clamped
   // into the row), so they cost one memory round trip, not one each. Only a
@@ -515,7 +671,11 @@ split_kernel(SplitArgs a) {
   // microseconds to every workgroup that issues them.
   uint64_t tbits = ~0ull;
   auto load_mask = [&]() {
-    const uint8_t* mrow = a.tree_mask + ((int64_t)b * a.Q + rr / a.H) * a.Q;
+    // (the divisor goes through an opaque move, so that the division's setup
+    // is not hoisted out of the loop over pieces and kept live through it)
+    int heads;
+    asm volatile("s_mov_b32 %0, %1" : "=s"(heads) : "s"(a.H));
+    const uint8_t* mrow = a.tree_mask + ((int64_t)b * a.Q + rr / heads) * a.Q;
     uint64_t bits = 0;
     for (int t0 = 0; t0 < a.Q; t0 += 16) {
       uint32_t mb[16];
@@ -533,7 +693,7 @@ split_kernel(SplitArgs a) {
   // Loading and placing are separate steps, so that a wave can have other
   // loads in flight with the queries.
   bf16x8 qf[kRegKSteps];
-  LDS_AS char* my_q = lds + kOffQPark + wave * kQParkBytes + lane * 16;
+  LDS_AS char* my_q;
   auto load_q = [&](u32x4 (&qv)[kHalfKSteps]) {
     const u32x4* qrow = reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * a.R + rr) * kLatent) +
                         p * (kHalfKSteps * 2) + h;
@@ -577,8 +737,8 @@ split_kernel(SplitArgs a) {
 #pragma unroll
       for (int d = 0; d < 2; ++d) tr_addr[hf][d] = (unsigned)(uintptr_t)tile + (unsigned)value_off(t00, hf, d);
   };
-  LDS_AS char* xchg = lds + kOffXchg + pair * kXchgBytes + lane * 16;   // + k * 1024
-  LDS_AS char* pbuf = lds + kOffP + lane * 16;                          // + rb * kPBytes + t * 1024
+  LDS_AS char* xchg;   // lds + kOffXchg + pair * kXchgBytes + lane * 16, + k * 1024
+  LDS_AS char* pbuf;   // lds + kOffP + lane * 16, + rb * kPBytes + t * 1024
   LDS_AS char* abuf = lds + kOffAlpha;
   LDS_AS char* fbuf = lds + kOffFlag;
 
@@ -599,7 +759,7 @@ split_kernel(SplitArgs a) {
   auto tile_key_ok = [&](int v, int gkey) -> bool { return kstart + (int64_t)v * kUnit + gkey < kend; };
   auto load_slots_to_lds = [&](int v) {
     if (wave == 4) {
-      int64_t gpos = sbase + kstart + (int64_t)v * kUnit + (lane & 31);
+      int64_t gpos = sbase + kstart + (int64_t)v * kUnit + (fresh_lane() & 31);
       gpos = gpos < a.total_kv ? gpos : a.total_kv - 1;
       gpos = gpos < 0 ? 0 : gpos;
       lds_dma4(a.kv_indices + gpos, slot_ring + (v % kSlotRing) * 256);
@@ -744,7 +904,7 @@ split_kernel(SplitArgs a) {
     float mx = x[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, x[i]);
-    mx = fmaxf(mx, swap_halves(mx));
+    mx = fmaxf(mx, swap_halves(mx, swap_addr));
     const bool grow = mx > m_ref + kLazyRescale;  // false while the row has seen nothing
     const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.f;  // exp2(-inf) = 0
     if (grow) m_ref = mx;
@@ -763,7 +923,7 @@ split_kernel(SplitArgs a) {
     *reinterpret_cast<LDS_AS f16x8*>(pbuf_of(u) + pair * kPBytes + 1024) = p1;
     const int any_grow = __ballot(grow) != 0;  // wave-wide: taken before any lane is masked off
     if (h == 0) *reinterpret_cast<LDS_AS float*>(abuf_of(u) + (pair * 32 + n) * 4) = alpha;
-    if (lane == 0) *reinterpret_cast<LDS_AS uint8_t*>(fbuf_of(u) + pair) = (uint8_t)any_grow;
+    if (fresh_lane() == 0) *reinterpret_cast<LDS_AS uint8_t*>(fbuf_of(u) + pair) = (uint8_t)any_grow;
   };
   // ---- this wave's value operands of one tile: V^T for its two 32-dim
   // blocks and both 16-key steps, transposed and converted to fp16.
@@ -929,22 +1089,67 @@ split_kernel(SplitArgs a) {
       apply_values(nunits - 1, vheld);
     }
   };
+  for (int piece = 0;;) {
+    if (piece > 0) {
+      // Piece `piece` of the column (column plan): sequence b0 + piece from
+      // its first key; its tiles start past those of the pieces before it.
+      const int b0 = __builtin_amdgcn_readfirstlane((int)plan_st[0]);
+      int64_t sb = uniform64(plan_st[2]);
+      int64_t ub = uniform64(plan_st[3]);
+      for (int j = 0; j < piece; ++j) {
+        int64_t pl = a.prefix_lens[b0 + j];
+        pl = pl < 0 ? 0 : (pl > a.total_kv ? a.total_kv : pl);
+        sb += pl + a.Q;
+        ub += (pl + a.Q + kUnit - 1) / kUnit + kSeqUnits;
+      }
+      b = b0 + piece;
+      c = __builtin_amdgcn_readfirstlane((int)plan_st[1]) + piece;
+      sbase = sb;
+      int64_t pl = a.prefix_lens[b];
+      pl = pl < 0 ? 0 : (pl > a.total_kv ? a.total_kv : pl);
+      P = uniform64(pl);
+      kstart = 0;
+      kend = uniform64((uniform64(plan_st[4]) - ub) * kUnit);
+    }
+    lane = fresh_lane();
+    n = lane & 31;
+    h = lane >> 5;
+    swap_addr = (lane ^ 32) << 2;
+    row_ok = row_of_lane() < a.R;
+    rr = row_ok ? row_of_lane() : 0;
+    my_q = lds + kOffQPark + wave * kQParkBytes + lane * 16;
+    xchg = lds + kOffXchg + pair * kXchgBytes + lane * 16;
+    pbuf = lds + kOffP + lane * 16;
+    if (kend > P + a.Q) kend = P + a.Q;
+    if (kend > a.total_kv - sbase) kend = a.total_kv - sbase;  // positions past the array are absent
+    nunits = kend > kstart ? (int)((kend - kstart + kUnit - 1) / kUnit) : 0;
+    tbits = ~0ull;
+    m_ref = -INFINITY;
+    l_sum = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < kRowBlocks; ++rb)
+#pragma unroll
+      for (int db = 0; db < kWaveDvBlocks; ++db) o[rb][db] = f32x16{};
+
   if (p == 0) run(IntC<0>{});
   else run(IntC<1>{});
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing gathers and slot copies before exit
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the trailing gathers and slot copies
 
   // ---- epilogue: the even halves publish 1/l per row (reusing the alpha
   // slots) and write lse; every wave normalises and writes its 64 dims.
   {
-    const float l_tot = l_sum + swap_halves(l_sum);
+    // (lane values re-derived, as elsewhere in the loop over pieces)
+    const int efl = fresh_lane();
+    const int en = efl & 31, eh = efl >> 5;
+    const float l_tot = l_sum + swap_halves(l_sum, (efl ^ 32) << 2);
     const bool live = l_tot > 0.f;
     asm volatile("s_barrier" ::: "memory");  // all waves are past their last alpha read
     if (p == 0) {
-      if (h == 0) *reinterpret_cast<LDS_AS float*>(abuf + (pair * 32 + n) * 4) = live ? 1.f / l_tot : 0.f;
+      if (eh == 0) *reinterpret_cast<LDS_AS float*>(abuf + (pair * 32 + en) * 4) = live ? 1.f / l_tot : 0.f;
       const float lse_v = live ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
       // the row index is re-derived here rather than kept live through the loop
-      const int r2 = rt * kRowsPerWG + pair * 32 + (fresh_lane() & 31);
-      if (r2 < a.R && h == 0) a.part_lse[(int64_t)c * a.R + r2] = lse_v;
+      const int r2 = rt * kRowsPerWG + pair * 32 + en;
+      if (r2 < a.R && eh == 0) a.part_lse[(int64_t)c * a.R + r2] = lse_v;
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     // The normalised block is rounded to fp16 (|O / l| is at most the largest
@@ -956,7 +1161,7 @@ split_kernel(SplitArgs a) {
     LDS_AS char* stg = lds + wave * kStageBytes;
 #pragma unroll
     for (int rb = 0; rb < kRowBlocks; ++rb) {
-      const float inv = *reinterpret_cast<LDS_AS const float*>(abuf + (rb * 32 + n) * 4);
+      const float inv = *reinterpret_cast<LDS_AS const float*>(abuf + (rb * 32 + en) * 4);
 #pragma unroll
       for (int db = 0; db < kWaveDvBlocks; ++db)
 #pragma unroll
@@ -964,18 +1169,25 @@ split_kernel(SplitArgs a) {
           f16x4 hv;
 #pragma unroll
           for (int e = 0; e < 4; ++e) hv[e] = (_Float16)(o[rb][db][4 * qd + e] * inv);
-          *reinterpret_cast<LDS_AS f16x4*>(stg + n * kStageRow + (db * 32 + 8 * qd + 4 * h) * 2) = hv;
+          *reinterpret_cast<LDS_AS f16x4*>(stg + en * kStageRow + (db * 32 + 8 * qd + 4 * eh) * 2) = hv;
         }
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int row = 8 * k + (lane >> 3);
-        const int ch = lane & 7;
+        const int fl = fresh_lane();
+        const int row = 8 * k + (fl >> 3);
+        const int ch = fl & 7;
         const u32x4 v = *reinterpret_cast<LDS_AS const u32x4*>(stg + row * kStageRow + ch * 16);
         const int rw = rt * kRowsPerWG + rb * 32 + row;
         if (rw < a.R)
           *reinterpret_cast<u32x4*>(a.part_o + ((int64_t)c * a.R + rw) * kValue + wave * kWaveDvBlocks * 32 + ch * 8) = v;
       }
     }
+  }
+
+    if (++piece >= __builtin_amdgcn_readfirstlane((int)plan_st[5])) break;
+    // Every wave is done with the epilogue's LDS (staging in the tile ring, the
+    // 1/l slots) before the next prologue refills the ring.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
 }
 

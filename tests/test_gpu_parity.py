@@ -260,32 +260,43 @@ def test_random_shape_sweep(env, case):
 
 
 def _plan_model(w, plan, ncu):
-    """The chunk plan's rule written out plainly: one chunk length L for the batch,
-    the smallest multiple of 32 not below the host's shortest length for which the
-    batch needs at most CUs / row_tiles chunks (sought only when there are fewer
-    sequences than that budget, and at most 512), by brute force here; chunk
-    offsets are the running sum of ceil(N_b / L), N_b = clamped prefix + Q,
-    capped at the partial buffers' capacity."""
+    """The split plan's piece offsets written out plainly. With fewer sequences than
+    the budget of CUs / row_tiles columns (and at most 512): lay every sequence's
+    32-key tiles end to end, each preceded by 3 units standing for a piece's
+    start-up, cut the axis of U units into columns of ceil(U / C) units (C = the
+    budget, at most max_chunks - B + 1 and at most the launched columns), and give
+    a sequence one piece per column its tiles meet.
+    Otherwise every chunk of the host's length is a piece. Offsets are running sums
+    of pieces per sequence, capped at the partial buffers' capacity."""
     n = np.clip(w.prefix_lens.astype(np.int64), 0, w.total_kv) + w.Q
     budget = max(1, ncu // plan["row_tiles"])
-    count = lambda length: int(np.sum(-(-n // length)))  # noqa: E731
-    length = plan["chunk_keys"]
     if budget > w.B and w.B <= 512:
-        while count(length) > budget:
-            length += 32
-    off = np.concatenate([[0], np.cumsum(-(-n // length))])
-    return np.minimum(off, plan["max_chunks"]).astype(np.int32), length
+        tiles = -(-n // 32)
+        units_end = np.cumsum(tiles + 3)
+        first_tile = units_end - tiles
+        U = int(units_end[-1])
+        C = max(1, min(budget, plan["max_chunks"] - w.B + 1, plan["grid"] // plan["row_tiles"]))
+        width = -(-U // C)
+        pieces = (units_end - 1) // width - first_tile // width + 1
+        desc = f"{C} columns"
+    else:
+        pieces = -(-n // plan["chunk_keys"])
+        desc = f"chunks of {plan['chunk_keys']} keys"
+    off = np.concatenate([[0], np.cumsum(pieces)])
+    return np.minimum(off, plan["max_chunks"]).astype(np.int32), desc
 
 
 @pytest.mark.parametrize("label,B,Q,H,prefix", [
     ("batch600_two_scan_passes", 600, 2, 4, (0, 60)),    # more sequences than the budget; two scan passes
     ("batch300_over_budget", 300, 3, 4, (0, 80)),         # more sequences than the budget; one pass
-    ("batch100_length_search", 100, 4, 2, (696, 696)),    # the shortest length needs 300 chunks: searched
-    ("batch8_ragged_search", 8, 4, 2, (4000, 30000)),     # ragged lengths, searched
+    ("batch100_columns", 100, 4, 2, (696, 696)),          # equal sequences, 256 columns
+    ("batch8_ragged_columns", 8, 4, 2, (4000, 30000)),    # ragged lengths: columns cross sequences
+    ("batch40_short_columns", 40, 4, 64, (0, 300)),       # several short sequences per column
+    ("batch2_uneven_columns", 2, 16, 64, (100, 60000)),   # one short, one long sequence
 ])
 def test_chunk_plan_batches(env, label, B, Q, H, prefix):
-    """Large and ragged batches through the chunk plan that every split workgroup
-    computes for itself: parity with the oracle, and the chunk offsets that
+    """Large and ragged batches through the split plan that every split workgroup
+    computes for itself: parity with the oracle, and the piece offsets that
     workgroup 0 leaves at the start of the workspace for the merge (int32 [B+1])
     equal the rule's."""
     torch, va = env
@@ -296,10 +307,9 @@ def test_chunk_plan_batches(env, label, B, Q, H, prefix):
     ws.fill_(0xFF)
     _check(env, w, label=label, workspace=ws)
     got = ws[: 4 * (B + 1)].cpu().numpy().view(np.int32)
-    want, length = _plan_model(w, plan, torch.cuda.get_device_properties(0).multi_processor_count)
-    print(f"[parity] {label}: chunk length {length} (shortest allowed {plan['chunk_keys']}), "
-          f"{want[-1]} chunks", flush=True)
-    assert np.array_equal(got, want), f"{label}: chunk offsets differ from the plan rule"
+    want, desc = _plan_model(w, plan, torch.cuda.get_device_properties(0).multi_processor_count)
+    print(f"[parity] {label}: {desc}, {want[-1]} pieces", flush=True)
+    assert np.array_equal(got, want), f"{label}: piece offsets differ from the plan rule"
 
 
 def test_defragmented_cache_full_size_bitwise_equal(env):
