@@ -666,8 +666,8 @@ split_kernel(SplitArgs a) {
   // Tail-visibility bits of the lane's query (even half; all ones elsewhere).
   // The first 16 positions are 16 unconditional byte loads (indices clamped
   // into the row), so they cost one memory round trip, not one each. Only a
-  // chunk that reaches the tail (kend > P) consults them, and only such a
-  // chunk loads them: at the start of a launch the byte loads add about two
+  // piece that reaches the tail (kend > P) consults them, and only such a
+  // piece loads them: at the start of a launch the byte loads add about two
   // microseconds to every workgroup that issues them.
   uint64_t tbits = ~0ull;
   auto load_mask = [&]() {
