@@ -57,12 +57,14 @@ size_t verify_attn_workspace_size_ex(int B, int Q, int H, int64_t total_kv, int3
 
 /*
  * The split plan verify_attn_ex() would use for these sizes and this
- * chunk_keys (0 = automatic) on the current device: the shortest keys per
- * chunk (with chunk_keys = 0 the device may pick a longer length, the
- * shortest whose chunks fit in the chunk budget of the grid, from the actual
- * prefix lengths), the chunk capacity of the workspace, row tiles per
- * sequence (128 query-head rows each) and the split-kernel grid size. Any
- * output pointer may be NULL. Returns VA_OK or VA_EINVAL.
+ * chunk_keys (0 = automatic) on the current device: the keys per chunk (with
+ * chunk_keys = 0, the keys per column at which the columns fill the grid; the
+ * device then cuts the batch's key tiles into equal columns from the actual
+ * prefix lengths when there are fewer sequences than columns, and into
+ * chunks of this length otherwise), the capacity of the workspace in pieces
+ * (one partial each), row tiles per sequence (128 query-head rows each) and
+ * the split-kernel grid size. Any output pointer may be NULL. Returns VA_OK
+ * or VA_EINVAL.
  */
 int verify_attn_query_plan(int B, int Q, int H, int64_t total_kv, int32_t chunk_keys_in,
                            int32_t* chunk_keys, int32_t* max_chunks, int32_t* row_tiles,
