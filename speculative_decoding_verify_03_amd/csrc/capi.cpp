@@ -85,27 +85,31 @@ bool make_plan(int B, int Q, int H, int64_t total_kv, int ncu, int32_t chunk_key
   ideal = (ideal + va::kUnit - 1) / va::kUnit * va::kUnit;
   p->target = ov > 0 ? 0 : (int32_t)target;   // a forced length is used as is
   p->ideal_keys = (int32_t)ideal;
-  // Partial buffers: a sequence of N_b keys takes ceil(N_b / ideal) chunks,
-  // so the chunk plan never needs more than total_kv / ideal + B of them; the
-  // column plan uses at most max_chunks - B + 1 columns, and so at most
-  // max_chunks pieces.
-  const int64_t max_chunks = total_kv / ideal + B + 1;
-  if (max_chunks > INT32_MAX / 8) return false;
-  p->max_chunks = (int32_t)max_chunks;
   // Workgroups: the row tiles of every column, rounded up to whole groups of
-  // 8 columns (the XCD mapping). The column plan (a budget above B, at most
-  // kPlanThreads sequences) uses at most `target` columns, and no more than
-  // are launched; a batch of one sequence is given at most
-  // ceil((total_kv + Q) / ideal) of them (pieces of about ideal keys).
-  // Launching no workgroup beyond these bounds matters because a surplus
-  // workgroup only gets a compute unit once a working one has finished, and
-  // then adds its own start-up to the end of the launch.
-  int64_t live = max_chunks;
+  // 8 columns (the XCD mapping): at most one column per ideal keys, plus one
+  // per sequence (the chunk plan's count), at most ceil((total_kv + Q) / ideal)
+  // for a batch of one sequence, and at most `target` under the column plan
+  // (a budget above B, at most kPlanThreads sequences), which uses no more
+  // columns than are launched. Launching no workgroup beyond these bounds
+  // matters because a surplus workgroup only gets a compute unit once a
+  // working one has finished, and then adds its own start-up to the end of
+  // the launch.
+  const bool columns = p->target > B && B <= va::kPlanThreads;
+  const int64_t chunk_bound = total_kv / ideal + B + 1;
+  int64_t live = chunk_bound;
   if (B == 1) live = std::min<int64_t>(live, (total_kv + Q + ideal - 1) / ideal);
-  if (p->target > B && B <= va::kPlanThreads) live = std::min<int64_t>(live, p->target);
-  const int64_t grid = (live + 7) / 8 * 8 * p->row_tiles;
+  if (columns) live = std::min<int64_t>(live, p->target);
+  const int64_t launched = (live + 7) / 8 * 8;
+  const int64_t grid = launched * p->row_tiles;
   if (grid > INT32_MAX) return false;
   p->grid = (int32_t)grid;
+  // Partial buffers: a sequence of N_b keys takes ceil(N_b / ideal) chunks,
+  // so the chunk plan never needs more than total_kv / ideal + B of them; the
+  // column plan's pieces are at most its columns + B - 1.
+  int64_t max_chunks = chunk_bound;
+  if (columns) max_chunks = std::max<int64_t>(max_chunks, launched + B);
+  if (max_chunks > INT32_MAX / 8) return false;
+  p->max_chunks = (int32_t)max_chunks;
   size_t off = 0;
   p->off_chunk = off;
   off += sizeof(int32_t) * (size_t)(B + 1);

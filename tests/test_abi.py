@@ -79,24 +79,28 @@ def test_bad_arguments_rejected_before_launch(lib, over, code):
 
 
 def test_plan_grid_covers_every_chunk(lib):
-    """The grid gives row_tiles workgroups to every chunk the device plan can
-    produce, rounded up to groups of 8 chunks: at most the partial buffers'
-    capacity; for one sequence at most ceil((total_kv + Q) / chunk_keys) (its N is
-    at most total_kv + Q and its chunk length at least chunk_keys); and, when the
-    plan searches a chunk length (a budget of CUs / row_tiles chunks above B), at
-    most that budget."""
+    """The grid gives row_tiles workgroups to every column the device plan can
+    use, rounded up to groups of 8: at most one per chunk_keys keys plus one per
+    sequence; for one sequence at most ceil((total_kv + Q) / chunk_keys); and under
+    the column plan (a budget of CUs / row_tiles columns above B) at most that
+    budget. The partial buffers then hold every piece: total_kv / chunk_keys + B + 1
+    chunks, and under the column plan the launched columns + B pieces."""
     for B, Q, H, T, ck in [(1, 16, 64, 185016, 0), (1, 16, 8, 185016, 0), (1, 16, 64, 4112, 0),
                            (1, 8, 16, 3008, 32), (1, 4, 8, 260, 0), (8, 8, 64, 528448, 0), (3, 4, 40, 6512, 32),
-                           (600, 4, 8, 700000, 0)]:
+                           (600, 4, 8, 700000, 0), (3, 1, 8, 18, 0), (250, 4, 2, 8000, 0)]:
         p = va.query_plan(B, Q, H, T, chunk_keys=ck)
         L = p["chunk_keys"]
-        need = p["max_chunks"]
+        bound = T // L + B + 1
+        need = bound
         if B == 1:
             need = min(need, -(-(T + Q) // L))
         budget = 256 // p["row_tiles"] if ck == 0 else 0   # 256 CUs: MI355X, and the plan's value without a device
-        if budget > B:
+        columns = budget > B and B <= 512
+        if columns:
             need = min(need, budget)
-        assert p["grid"] == -(-need // 8) * 8 * p["row_tiles"], (B, Q, H, T, ck, p)
+        launched = -(-need // 8) * 8
+        assert p["grid"] == launched * p["row_tiles"], (B, Q, H, T, ck, p)
+        assert p["max_chunks"] == (max(bound, launched + B) if columns else bound), (B, Q, H, T, ck, p)
 
 
 def test_debug_gather_argument_checks(lib):

@@ -293,6 +293,8 @@ def _plan_model(w, plan, ncu):
     ("batch8_ragged_columns", 8, 4, 2, (4000, 30000)),    # ragged lengths: columns cross sequences
     ("batch40_short_columns", 40, 4, 64, (0, 300)),       # several short sequences per column
     ("batch2_uneven_columns", 2, 16, 64, (100, 60000)),   # one short, one long sequence
+    ("batch250_columns", 250, 4, 2, (0, 60)),             # just under the budget: many pieces per column
+    ("batch3_tiny_columns", 3, 1, 8, (0, 10)),            # fewer axis units than columns
 ])
 def test_chunk_plan_batches(env, label, B, Q, H, prefix):
     """Large and ragged batches through the split plan that every split workgroup
