@@ -259,6 +259,34 @@ def test_random_shape_sweep(env, case):
     _check(env, w, label=f"sweep{i}", chunk_keys=chunk)
 
 
+def _column_sweep_cases(n=12, seed=913):
+    """Seeded random batches under the automatic plan (the column plan): up to 40
+    sequences of ragged lengths, some empty and some a single tile, so that columns
+    cross sequence boundaries, hold several short sequences, or start inside a
+    sequence's start-up units."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        B = int(rng.integers(2, 41))
+        Q = int(rng.integers(1, 9))
+        H = int(rng.integers(1, 33))
+        hi = [40, 600, 3000][i % 3]
+        prefix = [int(x) for x in rng.integers(0, hi, size=B)]
+        prefix[int(rng.integers(0, B))] = 0
+        mask = ["chain", "tree"][i % 2]
+        cases.append((i, B, Q, H, prefix, mask))
+    return cases
+
+
+@pytest.mark.parametrize("case", _column_sweep_cases(), ids=lambda c: f"columns{c[0]}")
+def test_column_plan_sweep(env, case):
+    i, B, Q, H, prefix, mask = case
+    w = make_workload(f"columns{i}", [914, i], B=B, Q=Q, H=H, prefix_lens=prefix, mask=mask,
+                      num_slots=sum(prefix) + B * Q + 64)
+    print(f"[parity] columns{i}: B={B} Q={Q} H={H} prefix sum={sum(prefix)} mask={mask}", flush=True)
+    _check(env, w, label=f"columns{i}")
+
+
 def _plan_model(w, plan, ncu):
     """The split plan's piece offsets written out plainly. With fewer sequences than
     the budget of CUs / row_tiles columns (and at most 512): lay every sequence's
