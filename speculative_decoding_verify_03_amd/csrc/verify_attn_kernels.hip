@@ -414,6 +414,37 @@ __device__ __forceinline__ int32_t wave_scan_dpp(int32_t x) {
 // lengths need not add up to total_kv); a column's units and its pieces fit
 // in 32 bits.
 __device__ ChunkPlan column_plan(const SplitArgs& a, int g, bool write_offsets, LDS_AS char* scratch) {
+  int C = a.max_chunks - a.B + 1;                   // pieces fit the partial buffers
+  if (C > a.target) C = a.target;                   // one wave of workgroups
+  const int launched = (int)(gridDim.x / a.row_tiles);
+  if (C > launched) C = launched;                   // every column has its workgroups
+  if (C < 1) C = 1;
+  if (a.B == 1) {
+    // One sequence: the same rule in closed form, with no scans and no
+    // barriers (its tiles start at unit kSeqUnits; the axis ends after them).
+    int64_t pl = a.prefix_lens[0];
+    pl = pl < 0 ? 0 : (pl > a.total_kv ? a.total_kv : pl);
+    const int64_t U = kSeqUnits + (pl + a.Q + kUnit - 1) / kUnit;
+    const int64_t W = (U + C - 1) / C;
+    const int64_t cs = kSeqUnits / W, ce = (U - 1) / W;
+    if (write_offsets && threadIdx.x == 0) {
+      a.chunk_off[0] = 0;
+      a.chunk_off[1] = (int32_t)(ce - cs + 1);
+    }
+    ChunkPlan cp;
+    const bool meets = cs <= g && g <= ce;
+    cp.b = 0;
+    cp.c = (int32_t)(g - cs);
+    cp.nseg = meets ? 1 : 0;
+    cp.sbase = 0;
+    cp.P = pl;
+    cp.ubase = kSeqUnits;
+    const int64_t lo = (int64_t)g * W;
+    cp.uend = lo + W < U ? lo + W : U;
+    cp.kstart = ((lo > cp.ubase ? lo : cp.ubase) - cp.ubase) * kUnit;
+    cp.kend = (cp.uend - cp.ubase) * kUnit;
+    return cp;
+  }
   LDS_AS int64_t* wu = reinterpret_cast<LDS_AS int64_t*>(scratch);   // 8 wave totals of units
   LDS_AS int64_t* wn = wu + 8;                                       // 8 wave totals of keys
   LDS_AS int32_t* wp = reinterpret_cast<LDS_AS int32_t*>(wu + 16);   // 8 wave totals of pieces
@@ -454,11 +485,6 @@ __device__ ChunkPlan column_plan(const SplitArgs& a, int g, bool write_offsets, 
 
   // Columns: column j covers units [j W, min((j + 1) W, U)) with W =
   // ceil(U / C), so unit x lies in column x / W.
-  int C = a.max_chunks - B + 1;                     // pieces fit the partial buffers
-  if (C > a.target) C = a.target;                   // one wave of workgroups
-  const int launched = (int)(gridDim.x / a.row_tiles);
-  if (C > launched) C = launched;                   // every column has its workgroups
-  if (C < 1) C = 1;
   const int64_t W = (U + C - 1) / C;                // uniform: one division
   const bool small = U < ((int64_t)1 << 31);        // always, when the lengths fit the array
   auto col = [&](int64_t x) -> int32_t {
