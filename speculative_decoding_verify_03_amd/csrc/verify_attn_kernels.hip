@@ -798,7 +798,9 @@ split_kernel(SplitArgs a) {
   };
   auto load_slot = [&](int v) -> int32_t {
     const int64_t pos = kstart + (int64_t)v * kUnit + glane().key;
-    return pos < kend ? a.kv_indices[sbase + pos] : -1;
+    int64_t gpos = sbase + pos;   // inside [0, total_kv) for pos < kend; clamped all the same
+    gpos = gpos < 0 ? 0 : (gpos >= a.total_kv ? a.total_kv - 1 : gpos);
+    return pos < kend ? a.kv_indices[gpos] : -1;
   };
   auto issue = [&](int32_t slot, LDS_AS char* tile) { issue_tile_gather(a.kv_pool, a.num_slots, slot, tile, glane()); };
 
