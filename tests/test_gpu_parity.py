@@ -52,6 +52,16 @@ def test_config_full_size_whole_output(env, name):
     _check(env, make_config(name))
 
 
+def test_batch48_column_plan_whole_output(env):
+    """48 sequences of 500 to 8000 keys at 64 heads and 8 verify positions (about
+    200k keys; 4 row tiles, so a budget of 64 columns for 48 sequences: the column
+    plan at scale: 110 pieces over 64 columns), whole output against
+    the oracle."""
+    w = make_workload("batch48_mixed", [915, 48], B=48, Q=8, H=64, prefix_range=(500, 8000), mask="tree")
+    print(f"[parity] start batch48_mixed: total_kv={w.total_kv}", flush=True)
+    _check(env, w, label="batch48_mixed")
+
+
 EDGE_CASES = {
     "no_prefix": dict(B=1, Q=16, H=8, prefix_lens=[0], mask="chain", num_slots=64),
     "single_query": dict(B=1, Q=1, H=16, prefix_lens=[1000], mask="chain", num_slots=4096),
